@@ -1,0 +1,292 @@
+"""ctypes binding of the C ABI declared in ``include/sparse_attn.h``.
+
+Argument marshalling only: every step of the attention runs in the HIP
+library.  PyTorch supplies device memory (``torch.empty``) and the current
+stream.  The library is loaded on first use; if it has not been built the
+call raises (there is no fallback).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libsparse_attn.so"
+
+# enum values of sparse_attn.h
+SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ESIZE, SA_EHIP = 0, -1, -2, -3, -4
+KINDS = {"local": 0, "stride": 1, "sameblock": 2, "summary": 3}
+SA_BF16, SA_FP32 = 0, 1
+SA_SELF_IF_EMPTY = 1
+SA_BLOB_MAGIC = 0x31415053
+SA_TILE_PARTIAL, SA_TILE_FULL = 0, 1
+
+EXPORTED = (
+    "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd",
+    "sparse_attn_bwd_workspace", "sparse_attn_bwd", "sparse_attn_strerror",
+)
+
+
+class CHeadPattern(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("l", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("sub", ctypes.c_int32)]
+
+
+class CLayoutDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("heads", ctypes.POINTER(CHeadPattern)),
+                ("flags", ctypes.c_uint32)]
+
+
+class CPatternRec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("l", ctypes.c_int32), ("c", ctypes.c_int32),
+                ("sub", ctypes.c_int32), ("s", ctypes.c_int32), ("nnz", ctypes.c_int32),
+                ("pairs", ctypes.c_int64)] + [
+        (f, ctypes.c_int64) for f in ("qmap_off", "kmap_off", "lo_off", "hi_off", "count_off",
+                                      "row_ptr_off", "col_off", "fflag_off", "col_ptr_off",
+                                      "row_off", "bflag_off")]
+
+
+class CBlobHeader(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("n", ctypes.c_int64),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_patterns", ctypes.c_int32),
+                ("n_pad", ctypes.c_int32), ("nqt", ctypes.c_int32), ("nkt", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("total_bytes", ctypes.c_int64),
+                ("head_pattern_off", ctypes.c_int64), ("pattern_off", ctypes.c_int64),
+                ("fwd_sched_off", ctypes.c_int64), ("bwd_sched_off", ctypes.c_int64),
+                ("fwd_sched_len", ctypes.c_int32), ("bwd_sched_len", ctypes.c_int32),
+                ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_strerror(status)} (status {status})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, LIB_NAME)
+
+
+def load_library():
+    """Load the built library (raises RuntimeError if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{LIB_NAME} is not built ({path}); run `python -m factorized_block_sparse_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.sparse_attn_layout.argtypes = [ctypes.POINTER(CLayoutDesc), vp, ctypes.POINTER(sz)]
+        lib.sparse_attn_layout.restype = i32
+        lib.sparse_attn_layout_check.argtypes = [vp, sz]
+        lib.sparse_attn_layout_check.restype = i32
+        lib.sparse_attn_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+        lib.sparse_attn_fwd.restype = i32
+        lib.sparse_attn_bwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.sparse_attn_bwd_workspace.restype = i32
+        lib.sparse_attn_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, sz, f32, vp]
+        lib.sparse_attn_bwd.restype = i32
+        lib.sparse_attn_strerror.argtypes = [i32]
+        lib.sparse_attn_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _strerror(status: int) -> str:
+    try:
+        return load_library().sparse_attn_strerror(status).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _check(rc: int, what: str):
+    if rc != SA_OK:
+        raise SparseAttnError(rc, what)
+
+
+@dataclass(frozen=True)
+class HeadPattern:
+    """One head's pattern: kind in {"local", "stride", "sameblock", "summary"}."""
+    kind: str
+    l: int
+    c: int = 0
+    sub: int = 0
+
+    def to_c(self) -> CHeadPattern:
+        if self.kind not in KINDS:
+            raise ValueError(f"unknown head kind {self.kind!r}")
+        return CHeadPattern(KINDS[self.kind], self.l, self.c, self.sub)
+
+
+def sparse_attn_layout(n: int, heads, block_q: int = 64, block_k: int = 64,
+                       self_if_empty: bool = True) -> np.ndarray:
+    """Build the layout blob (host bytes) for ``heads`` at sequence length ``n``."""
+    lib = load_library()
+    heads = [h if isinstance(h, HeadPattern) else HeadPattern(h.kind, h.l, h.c, h.sub) for h in heads]
+    arr = (CHeadPattern * max(1, len(heads)))(*[h.to_c() for h in heads])
+    desc = CLayoutDesc(n, block_q, block_k, len(heads), arr,
+                       SA_SELF_IF_EMPTY if self_if_empty else 0)
+    size = ctypes.c_size_t(0)
+    _check(lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)), "layout size")
+    blob = np.zeros(size.value, dtype=np.uint8)
+    _check(lib.sparse_attn_layout(ctypes.byref(desc), blob.ctypes.data_as(ctypes.c_void_p),
+                                  ctypes.byref(size)), "layout build")
+    return blob[: size.value]
+
+
+class Layout:
+    """A built layout: the host blob plus lazily made device copies (one per device)."""
+
+    def __init__(self, n: int, heads, block_q: int = 64, block_k: int = 64,
+                 self_if_empty: bool = True):
+        self.n = int(n)
+        self.heads = tuple(heads)
+        self.blob = sparse_attn_layout(n, heads, block_q, block_k, self_if_empty)
+        self.header = CBlobHeader.from_buffer_copy(self.blob[: ctypes.sizeof(CBlobHeader)].tobytes())
+        self._dev = {}
+
+    # -- host-side views (tests, accounting) --------------------------------
+    def _arr(self, off: int, count: int, dtype) -> np.ndarray:
+        nbytes = count * np.dtype(dtype).itemsize
+        return self.blob[off: off + nbytes].view(dtype)
+
+    @property
+    def num_patterns(self) -> int:
+        return self.header.num_patterns
+
+    def head_pattern_index(self) -> np.ndarray:
+        return self._arr(self.header.head_pattern_off, self.header.num_heads, np.int32)
+
+    def pattern_rec(self, i: int) -> CPatternRec:
+        off = self.header.pattern_off + i * ctypes.sizeof(CPatternRec)
+        return CPatternRec.from_buffer_copy(self.blob[off: off + ctypes.sizeof(CPatternRec)].tobytes())
+
+    def pattern_arrays(self, i: int) -> dict:
+        r, h = self.pattern_rec(i), self.header
+        return {
+            "qmap": self._arr(r.qmap_off, h.n_pad, np.int32),
+            "kmap": self._arr(r.kmap_off, h.n_pad, np.int32),
+            "lo": self._arr(r.lo_off, h.n_pad, np.int32),
+            "hi": self._arr(r.hi_off, h.n_pad, np.int32),
+            "count": self._arr(r.count_off, h.n, np.int32),
+            "row_ptr": self._arr(r.row_ptr_off, h.nqt + 1, np.int32),
+            "col": self._arr(r.col_off, r.nnz, np.int32),
+            "fflag": self._arr(r.fflag_off, r.nnz, np.uint8),
+            "col_ptr": self._arr(r.col_ptr_off, h.nkt + 1, np.int32),
+            "row": self._arr(r.row_off, r.nnz, np.int32),
+            "bflag": self._arr(r.bflag_off, r.nnz, np.uint8),
+        }
+
+    def fwd_schedule(self) -> np.ndarray:
+        return self._arr(self.header.fwd_sched_off, 2 * self.header.fwd_sched_len, np.int32).reshape(-1, 2)
+
+    def bwd_schedule(self) -> np.ndarray:
+        return self._arr(self.header.bwd_sched_off, 2 * self.header.bwd_sched_len, np.int32).reshape(-1, 2)
+
+    def pairs_per_batch(self) -> int:
+        """Visible (query, key) pairs summed over the heads of one batch element."""
+        return int(self.header.pairs_all_heads)
+
+    def tiles_per_batch(self) -> int:
+        return int(self.header.tiles_all_heads)
+
+    # -- device copy ---------------------------------------------------------
+    def device_blob(self, device):
+        import torch
+        dev = torch.device(device)
+        key = (dev.type, dev.index)
+        t = self._dev.get(key)
+        if t is None:
+            t = torch.from_numpy(self.blob.copy()).to(dev)
+            self._dev[key] = t
+        return t
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _check_qkv(layout: Layout, tensors, names):
+    import torch
+    ref = tensors[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, n, d]")
+    for t, nm in zip(tensors, names):
+        if not t.is_cuda:
+            raise ValueError(f"{nm} must be a GPU tensor")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError(f"{nm} must match q in shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    B, H, n, d = ref.shape
+    if n != layout.n or H != layout.header.num_heads:
+        raise ValueError(f"layout is for n={layout.n}, H={layout.header.num_heads}; got n={n}, H={H}")
+    if ref.dtype == torch.bfloat16:
+        dt = SA_BF16
+    elif ref.dtype == torch.float32:
+        dt = SA_FP32
+    else:
+        raise ValueError("dtype must be bfloat16 or float32")
+    return B, H, n, d, dt
+
+
+def sparse_attn_fwd(layout: Layout, q, k, v, scale: float | None = None, out=None, lse=None):
+    """Forward on the current torch stream: returns (o, lse)."""
+    import torch
+    lib = load_library()
+    B, H, n, d, dt = _check_qkv(layout, (q, k, v), ("q", "k", "v"))
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    blob_dev = layout.device_blob(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.sparse_attn_fwd(layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                             0.0 if scale is None else float(scale), stream)
+    _check(rc, "sparse_attn_fwd")
+    return o, lse_t
+
+
+def bwd_workspace_bytes(layout: Layout, B: int, H: int, d: int = 64, dtype: int = SA_BF16) -> int:
+    lib = load_library()
+    size = ctypes.c_size_t(0)
+    _check(lib.sparse_attn_bwd_workspace(layout.blob.ctypes.data, B, H, d, dtype,
+                                         ctypes.byref(size)), "sparse_attn_bwd_workspace")
+    return size.value
+
+
+def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = None,
+                    workspace=None, grads=None):
+    """Backward on the current torch stream: returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, n, d, dt = _check_qkv(layout, (q, k, v, o, do), ("q", "k", "v", "o", "do"))
+    if lse.shape != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+    need = bwd_workspace_bytes(layout, B, H, d, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    blob_dev = layout.device_blob(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.sparse_attn_bwd(layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                             0.0 if scale is None else float(scale), stream)
+    _check(rc, "sparse_attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,59 @@
+// Argument validation shared by the C ABI entry points (host code).
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+struct LaunchInfo {
+  int64_t n;
+  int32_t block_q, block_k, num_heads, n_pad, nqt, nkt;
+  int32_t fwd_sched_len, bwd_sched_len;
+  int64_t fwd_sched_off, bwd_sched_off, total_bytes;
+};
+
+inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks the blob and the shapes common to forward and backward; fills `li`.
+inline int validate_common(const void* blob_host, const void* blob_dev, int B, int H, int d,
+                           int dtype, LaunchInfo* li) {
+  if (!blob_host) return SA_EINVAL;
+  sa_blob_header h;
+  memcpy(&h, blob_host, sizeof(h));
+  if (h.magic != SA_BLOB_MAGIC || h.version != SA_BLOB_VERSION) return SA_EINVAL;
+  const int rc = sparse_attn_layout_check(blob_host, size_t(h.total_bytes));
+  if (rc != SA_OK) return rc;
+  if (!blob_dev || (reinterpret_cast<uintptr_t>(blob_dev) & 63u) != 0) return SA_EINVAL;
+  if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
+  if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
+  if (d != 64) return SA_EUNSUPPORTED;
+  // Element offsets of [B, H, n, d] must fit the kernels' 64-bit arithmetic and
+  // per-(b, h) 32-bit row indices.
+  if (int64_t(B) * H * h.n > (int64_t(1) << 40)) return SA_EUNSUPPORTED;
+  li->n = h.n;
+  li->block_q = h.block_q;
+  li->block_k = h.block_k;
+  li->num_heads = h.num_heads;
+  li->n_pad = h.n_pad;
+  li->nqt = h.nqt;
+  li->nkt = h.nkt;
+  li->fwd_sched_len = h.fwd_sched_len;
+  li->bwd_sched_len = h.bwd_sched_len;
+  li->fwd_sched_off = h.fwd_sched_off;
+  li->bwd_sched_off = h.bwd_sched_off;
+  li->total_bytes = h.total_bytes;
+  return SA_OK;
+}
+
+// scale <= 0 selects 1/sqrt(d) (blog post on sliding windows, section 01).
+inline int resolve_scale(float scale, int d, float* out) {
+  if (scale != scale || isinf(scale)) return SA_EINVAL;
+  *out = scale > 0.f ? scale : float(1.0 / sqrt(double(d)));
+  return SA_OK;
+}
+
+}  // namespace sa

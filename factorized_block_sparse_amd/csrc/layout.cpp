@@ -1,0 +1,427 @@
+// Host-side layout builder: head patterns -> per-pattern index maps, visible
+// key intervals, and the CSR / CSC lists of active (query-tile, key-tile)
+// pairs, packed into one position-independent blob.
+//
+// The visibility sets are those of "Sparse Transformers 深度解读报告",
+// section 2.2 (strided: local band and stride; fixed: same block and summary
+// columns), all causal (section 2.1).  Tile-level skipping follows report
+// section 3.5 and the block-sparse execution of the blog post on sliding
+// windows and block sparsity, section 05 (only tile pairs that contain a
+// visible pair are computed; a fine mask applies inside partial tiles).
+//
+// Each pattern is mapped to a "layout space" in which every query row reads a
+// single interval of key positions:
+//   local, same-block: identity order, interval [max(0,i-l), i] or [l*floor(i/l), i];
+//   stride: residue-class order (the grid-column view of the comparison
+//           article "稀疏与局部注意力", section 2), interval = the row's own
+//           class up to itself;
+//   summary: keys packed as the summary cells in order, so a row reads a
+//           prefix of them; rows that read nothing (before the first summary
+//           cell) read a key slot holding their own token.
+// This is what makes tiles dense for the stride and summary heads instead of
+// holding one useful key per row.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <tuple>
+#include <vector>
+
+#include "sparse_attn.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 26;
+constexpr int kMaxHeads = 4096;
+
+struct Pattern {
+  sa_head_pattern p{};
+  int32_t s = 0;
+  int64_t pairs = 0;
+  std::vector<int32_t> qmap, kmap, lo, hi, count;
+  std::vector<int32_t> row_ptr, col, col_ptr, row;
+  std::vector<uint8_t> fflag, bflag;
+};
+
+bool valid_tile(int32_t t) { return t == 32 || t == 64 || t == 128; }
+
+// Canonical form of a head pattern so that equal patterns share one record.
+sa_head_pattern canonical(const sa_head_pattern& h) {
+  sa_head_pattern c = h;
+  if (h.kind != SA_SUMMARY) {
+    c.c = 0;
+    c.sub = 0;
+  } else {
+    c.sub = h.sub % (h.l / h.c);
+  }
+  return c;
+}
+
+int check_head(const sa_head_pattern& h) {
+  if (h.kind < SA_LOCAL || h.kind > SA_SUMMARY) return SA_EINVAL;
+  if (h.l < 1) return SA_EINVAL;
+  if (h.kind == SA_SUMMARY) {
+    if (h.c < 1 || h.c > h.l || h.sub < 0) return SA_EINVAL;
+  }
+  return SA_OK;
+}
+
+// Index maps and intervals in layout space (see the header for the maps).
+int build_maps(Pattern& P, int64_t n64, int32_t n_pad, bool self_if_empty) {
+  const int32_t n = int32_t(n64);
+  const int32_t l = P.p.l;
+  P.qmap.assign(n_pad, -1);
+  P.kmap.assign(n_pad, -1);
+  P.lo.assign(n_pad, 1);
+  P.hi.assign(n_pad, 0);
+  P.count.assign(n, 0);
+  switch (P.p.kind) {
+    case SA_LOCAL:
+      for (int32_t i = 0; i < n; ++i) {
+        P.qmap[i] = P.kmap[i] = i;
+        P.lo[i] = i > l ? i - l : 0;
+        P.hi[i] = i;
+      }
+      break;
+    case SA_SAMEBLOCK:
+      for (int32_t i = 0; i < n; ++i) {
+        P.qmap[i] = P.kmap[i] = i;
+        P.lo[i] = (i / l) * l;
+        P.hi[i] = i;
+      }
+      break;
+    case SA_STRIDE: {
+      // Residue r holds ceil((n - r) / l) tokens; classes are laid out in order.
+      const int32_t classes = int32_t(std::min<int64_t>(l, n));
+      std::vector<int32_t> off(classes + 1, 0);
+      for (int32_t r = 0; r < classes; ++r) off[r + 1] = off[r] + (n - r + l - 1) / l;
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t r = i % l, t = i / l;
+        const int32_t p = off[r] + t;
+        P.qmap[p] = P.kmap[p] = i;
+        P.lo[p] = off[r];
+        P.hi[p] = p;
+      }
+      break;
+    }
+    case SA_SUMMARY: {
+      const int32_t c = P.p.c;
+      const int32_t s = l - (P.p.sub + 1) * c;
+      P.s = s;
+      std::vector<uint8_t> used(n, 0);
+      int32_t e = 0;
+      for (int64_t base = 0; base < n; base += l) {
+        for (int32_t u = 0; u < c; ++u) {
+          const int64_t j = base + s + u;
+          if (j < n) {
+            P.kmap[e++] = int32_t(j);
+            used[j] = 1;
+          }
+        }
+      }
+      for (int32_t i = 0; i < n; ++i) {
+        P.qmap[i] = i;
+        const int32_t rr = i % l - s + 1;
+        const int32_t cnt = (i / l) * c + std::min(std::max(rr, 0), c);
+        if (cnt > 0) {
+          P.lo[i] = 0;
+          P.hi[i] = cnt - 1;
+        } else {
+          if (!self_if_empty) return SA_EINVAL;  // empty row: no softmax
+          P.kmap[e] = i;
+          used[i] = 1;
+          P.lo[i] = P.hi[i] = e;
+          ++e;
+        }
+      }
+      for (int32_t j = 0; j < n; ++j)
+        if (!used[j]) P.kmap[e++] = j;
+      if (e != n) return SA_EINVAL;
+      break;
+    }
+    default:
+      return SA_EINVAL;
+  }
+  P.pairs = 0;
+  for (int32_t p = 0; p < n; ++p) {
+    const int32_t cnt = P.hi[p] - P.lo[p] + 1;
+    P.count[P.qmap[p]] = cnt;
+    P.pairs += cnt;
+  }
+  return SA_OK;
+}
+
+void build_tiles(Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
+  const int32_t nqt = n_pad / bq, nkt = n_pad / bk;
+  P.row_ptr.assign(nqt + 1, 0);
+  P.col.clear();
+  P.fflag.clear();
+  std::vector<uint8_t> mark(nkt, 0);
+  std::vector<int32_t> touched;
+  for (int32_t qt = 0; qt < nqt; ++qt) {
+    const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, n);
+    int32_t max_lo = INT32_MIN, min_hi = INT32_MAX;
+    touched.clear();
+    for (int32_t r = r0; r < r1; ++r) {
+      const int32_t lo = P.lo[r], hi = P.hi[r];
+      max_lo = std::max(max_lo, lo);
+      min_hi = std::min(min_hi, hi);
+      for (int32_t kt = lo / bk; kt <= hi / bk; ++kt) {
+        if (!mark[kt]) {
+          mark[kt] = 1;
+          touched.push_back(kt);
+        }
+      }
+    }
+    std::sort(touched.begin(), touched.end());
+    const bool rows_all_valid = (r0 + bq <= n);
+    for (int32_t kt : touched) {
+      const bool full = rows_all_valid && kt * bk >= max_lo && (kt + 1) * bk - 1 <= min_hi;
+      P.col.push_back(kt);
+      P.fflag.push_back(full ? SA_TILE_FULL : SA_TILE_PARTIAL);
+      mark[kt] = 0;
+    }
+    P.row_ptr[qt + 1] = int32_t(P.col.size());
+  }
+  // CSC by counting sort; rows come out ascending because CSR rows are visited in order.
+  const int32_t nnz = int32_t(P.col.size());
+  P.col_ptr.assign(nkt + 1, 0);
+  for (int32_t e = 0; e < nnz; ++e) P.col_ptr[P.col[e] + 1]++;
+  for (int32_t kt = 0; kt < nkt; ++kt) P.col_ptr[kt + 1] += P.col_ptr[kt];
+  P.row.assign(nnz, 0);
+  P.bflag.assign(nnz, 0);
+  std::vector<int32_t> fill(P.col_ptr.begin(), P.col_ptr.end() - 1);
+  for (int32_t qt = 0; qt < nqt; ++qt) {
+    for (int32_t e = P.row_ptr[qt]; e < P.row_ptr[qt + 1]; ++e) {
+      const int32_t dst = fill[P.col[e]]++;
+      P.row[dst] = qt;
+      P.bflag[dst] = P.fflag[e];
+    }
+  }
+}
+
+int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
+
+struct Writer {
+  uint8_t* base;  // NULL while sizing
+  int64_t pos = 0;
+  template <class T>
+  int64_t put(const T* data, size_t count) {
+    pos = align64(pos);
+    const int64_t at = pos;
+    if (base && count) std::memcpy(base + at, data, count * sizeof(T));
+    pos += int64_t(count * sizeof(T));
+    return at;
+  }
+  template <class T>
+  int64_t put(const std::vector<T>& v) {
+    return put(v.data(), v.size());
+  }
+};
+
+struct SchedItem {
+  int32_t head, tile, work;
+};
+
+std::vector<int32_t> sorted_schedule(std::vector<SchedItem> items) {
+  std::stable_sort(items.begin(), items.end(),
+                   [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
+  std::vector<int32_t> out;
+  out.reserve(items.size() * 2);
+  for (const auto& it : items) {
+    out.push_back(it.head);
+    out.push_back(it.tile);
+  }
+  return out;
+}
+
+int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
+  if (!desc || !blob_bytes) return SA_EINVAL;
+  if (desc->n < 1 || desc->n > kMaxN) return SA_EINVAL;
+  if (desc->num_heads < 1 || desc->num_heads > kMaxHeads || !desc->heads) return SA_EINVAL;
+  if (!valid_tile(desc->block_q) || !valid_tile(desc->block_k)) return SA_EUNSUPPORTED;
+  if (desc->flags & ~SA_SELF_IF_EMPTY) return SA_EINVAL;
+  const bool self_if_empty = (desc->flags & SA_SELF_IF_EMPTY) != 0;
+  const int32_t n = int32_t(desc->n);
+  const int32_t bq = desc->block_q, bk = desc->block_k;
+  const int32_t t = std::max(bq, bk);
+  const int32_t n_pad = int32_t(((desc->n + t - 1) / t) * t);
+  const int32_t nqt = n_pad / bq, nkt = n_pad / bk;
+
+  std::vector<Pattern> pats;
+  std::map<std::tuple<int32_t, int32_t, int32_t, int32_t>, int32_t> index;
+  std::vector<int32_t> head_pat(desc->num_heads);
+  for (int32_t h = 0; h < desc->num_heads; ++h) {
+    const int rc = check_head(desc->heads[h]);
+    if (rc != SA_OK) return rc;
+    const sa_head_pattern c = canonical(desc->heads[h]);
+    const auto key = std::make_tuple(c.kind, c.l, c.c, c.sub);
+    auto it = index.find(key);
+    if (it == index.end()) {
+      Pattern P;
+      P.p = c;
+      const int rc2 = build_maps(P, n, n_pad, self_if_empty);
+      if (rc2 != SA_OK) return rc2;
+      build_tiles(P, n, n_pad, bq, bk);
+      it = index.emplace(key, int32_t(pats.size())).first;
+      pats.push_back(std::move(P));
+    }
+    head_pat[h] = it->second;
+  }
+
+  std::vector<SchedItem> fwd_items, bwd_items;
+  int64_t pairs_all = 0, tiles_all = 0;
+  for (int32_t h = 0; h < desc->num_heads; ++h) {
+    const Pattern& P = pats[head_pat[h]];
+    pairs_all += P.pairs;
+    tiles_all += int64_t(P.col.size());
+    for (int32_t qt = 0; qt < nqt; ++qt) {
+      const int32_t w = P.row_ptr[qt + 1] - P.row_ptr[qt];
+      if (w > 0) fwd_items.push_back({h, qt, w});
+    }
+    for (int32_t kt = 0; kt < nkt; ++kt) {
+      if (kt * bk >= n) continue;  // all padding keys
+      bwd_items.push_back({h, kt, P.col_ptr[kt + 1] - P.col_ptr[kt] + 1});
+    }
+  }
+  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
+  const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
+
+  // Two passes: size, then write.
+  for (int pass = 0; pass < 2; ++pass) {
+    uint8_t* base = pass == 0 ? nullptr : blob;
+    Writer w{base};
+    sa_blob_header hdr{};
+    const int64_t hdr_at = w.put(&hdr, 1);
+    std::vector<sa_pattern_rec> recs(pats.size());
+    const int64_t rec_at = w.put(recs.data(), recs.size());
+    hdr.head_pattern_off = w.put(head_pat);
+    hdr.fwd_sched_off = w.put(fwd_sched);
+    hdr.bwd_sched_off = w.put(bwd_sched);
+    for (size_t i = 0; i < pats.size(); ++i) {
+      const Pattern& P = pats[i];
+      sa_pattern_rec& r = recs[i];
+      r.kind = P.p.kind;
+      r.l = P.p.l;
+      r.c = P.p.c;
+      r.sub = P.p.sub;
+      r.s = P.s;
+      r.nnz = int32_t(P.col.size());
+      r.pairs = P.pairs;
+      r.qmap_off = w.put(P.qmap);
+      r.kmap_off = w.put(P.kmap);
+      r.lo_off = w.put(P.lo);
+      r.hi_off = w.put(P.hi);
+      r.count_off = w.put(P.count);
+      r.row_ptr_off = w.put(P.row_ptr);
+      r.col_off = w.put(P.col);
+      r.fflag_off = w.put(P.fflag);
+      r.col_ptr_off = w.put(P.col_ptr);
+      r.row_off = w.put(P.row);
+      r.bflag_off = w.put(P.bflag);
+    }
+    const int64_t total = align64(w.pos);
+    if (pass == 0) {
+      if (!blob) {
+        *blob_bytes = size_t(total);
+        return SA_OK;
+      }
+      if (*blob_bytes < size_t(total)) {
+        *blob_bytes = size_t(total);
+        return SA_ESIZE;
+      }
+      std::memset(blob, 0, size_t(total));
+      continue;
+    }
+    hdr.magic = SA_BLOB_MAGIC;
+    hdr.version = SA_BLOB_VERSION;
+    hdr.n = desc->n;
+    hdr.block_q = bq;
+    hdr.block_k = bk;
+    hdr.num_heads = desc->num_heads;
+    hdr.num_patterns = int32_t(pats.size());
+    hdr.n_pad = n_pad;
+    hdr.nqt = nqt;
+    hdr.nkt = nkt;
+    hdr.flags = desc->flags;
+    hdr.total_bytes = total;
+    hdr.pattern_off = rec_at;
+    hdr.fwd_sched_len = int32_t(fwd_items.size());
+    hdr.bwd_sched_len = int32_t(bwd_items.size());
+    hdr.pairs_all_heads = pairs_all;
+    hdr.tiles_all_heads = tiles_all;
+    std::memcpy(blob + hdr_at, &hdr, sizeof(hdr));
+    std::memcpy(blob + rec_at, recs.data(), recs.size() * sizeof(sa_pattern_rec));
+    *blob_bytes = size_t(total);
+  }
+  return SA_OK;
+}
+
+bool in_blob(int64_t off, int64_t bytes, int64_t total) {
+  return off >= 0 && bytes >= 0 && off <= total && bytes <= total - off && (off % 4) == 0;
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_bytes) {
+  try {
+    return build(desc, static_cast<uint8_t*>(blob), blob_bytes);
+  } catch (...) {
+    return SA_EINVAL;  // allocation failure or similar: never throw across the ABI
+  }
+}
+
+extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes) {
+  if (!blob_host || blob_bytes < sizeof(sa_blob_header)) return SA_EINVAL;
+  const uint8_t* b = static_cast<const uint8_t*>(blob_host);
+  sa_blob_header h;
+  std::memcpy(&h, b, sizeof(h));
+  if (h.magic != SA_BLOB_MAGIC || h.version != SA_BLOB_VERSION) return SA_EINVAL;
+  const int64_t total = h.total_bytes;
+  if (total < int64_t(sizeof(h)) || size_t(total) > blob_bytes) return SA_ESIZE;
+  if (h.n < 1 || h.n > kMaxN || !valid_tile(h.block_q) || !valid_tile(h.block_k)) return SA_EINVAL;
+  if (h.num_heads < 1 || h.num_heads > kMaxHeads || h.num_patterns < 1 ||
+      h.num_patterns > h.num_heads)
+    return SA_EINVAL;
+  const int64_t t = std::max(h.block_q, h.block_k);
+  if (h.n_pad != ((h.n + t - 1) / t) * t || h.nqt * h.block_q != h.n_pad ||
+      h.nkt * h.block_k != h.n_pad)
+    return SA_EINVAL;
+  if (!in_blob(h.head_pattern_off, 4 * int64_t(h.num_heads), total) ||
+      !in_blob(h.pattern_off, int64_t(sizeof(sa_pattern_rec)) * h.num_patterns, total) ||
+      !in_blob(h.fwd_sched_off, 8 * int64_t(h.fwd_sched_len), total) ||
+      !in_blob(h.bwd_sched_off, 8 * int64_t(h.bwd_sched_len), total))
+    return SA_EINVAL;
+  for (int32_t i = 0; i < h.num_patterns; ++i) {
+    sa_pattern_rec r;
+    std::memcpy(&r, b + h.pattern_off + i * sizeof(sa_pattern_rec), sizeof(r));
+    const int64_t np = 4 * int64_t(h.n_pad);
+    if (!in_blob(r.qmap_off, np, total) || !in_blob(r.kmap_off, np, total) ||
+        !in_blob(r.lo_off, np, total) || !in_blob(r.hi_off, np, total) ||
+        !in_blob(r.count_off, 4 * h.n, total) ||
+        !in_blob(r.row_ptr_off, 4 * int64_t(h.nqt + 1), total) ||
+        !in_blob(r.col_off, 4 * int64_t(r.nnz), total) ||
+        !in_blob(r.col_ptr_off, 4 * int64_t(h.nkt + 1), total) ||
+        !in_blob(r.row_off, 4 * int64_t(r.nnz), total) || r.fflag_off < 0 ||
+        r.fflag_off + r.nnz > total || r.bflag_off < 0 || r.bflag_off + r.nnz > total)
+      return SA_EINVAL;
+  }
+  for (int32_t hh = 0; hh < h.num_heads; ++hh) {
+    int32_t p;
+    std::memcpy(&p, b + h.head_pattern_off + 4 * hh, 4);
+    if (p < 0 || p >= h.num_patterns) return SA_EINVAL;
+  }
+  return SA_OK;
+}
+
+extern "C" const char* sparse_attn_strerror(int status) {
+  switch (status) {
+    case SA_OK: return "success";
+    case SA_EINVAL: return "invalid argument";
+    case SA_EUNSUPPORTED: return "unsupported configuration";
+    case SA_ESIZE: return "buffer too small";
+    case SA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}

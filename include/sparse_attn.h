@@ -1,0 +1,189 @@
+/*
+ * sparse_attn.h -- C ABI of the causal factorized block-sparse attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Masked softmax attention (blog post "长序列为何不必让每个
+ * token 看见全部历史？滑动窗口、块稀疏与全局 token", section 02): with
+ * S_ij = scale * q_i . k_j over the keys j that query i may read,
+ *     O_i = sum_j softmax_j(S_ij) v_j,    LSE_i = log sum_j exp(S_ij),
+ * and its gradients.  The sets of keys come from the factorized heads of
+ * "Sparse Transformers 深度解读报告", section 2.2 (all causal, j <= i):
+ *     SA_LOCAL      strided head 1:  {max(0, i - l) .. i}
+ *     SA_STRIDE     strided head 2:  {j <= i : (i - j) mod l == 0}
+ *     SA_SAMEBLOCK  fixed head 1:    {j <= i : floor(j / l) == floor(i / l)}
+ *     SA_SUMMARY    fixed head 2:    {j <= i : s <= j mod l <= s + c - 1},
+ *                   s = l - (k + 1) c for sub-block k = sub mod (l / c)
+ * Rows left empty by a summary head (i < s) read only themselves when
+ * SA_SELF_IF_EMPTY is set (the default reading; without it such a layout is
+ * rejected, since an empty row has no softmax).  Execution is at tile
+ * granularity: only (query-tile, key-tile) pairs holding at least one
+ * visible pair are computed (report section 3.5; blog post section 05).
+ *
+ * Conventions.
+ *   - Tensors are contiguous [B, H, n, d] (batch, head, position, feature),
+ *     d innermost; LSE is [B, H, n] float32.  Head h uses the layout's
+ *     pattern of head h; H must equal the layout's num_heads.
+ *   - d must be 64.  dtype SA_BF16 (bfloat16 data, float32 accumulation)
+ *     for forward and backward; SA_FP32 (float32 throughout) for forward.
+ *   - Pointers q, k, v, o, lse, dO, dq, dk, dv and workspace are device
+ *     pointers (hipMalloc'd or equivalent) aligned to 16 bytes; blob_host is
+ *     a host pointer; blob_dev is a device copy of the same bytes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work and return without synchronising.
+ *
+ * Ownership.  The caller owns every buffer.  The library allocates and frees
+ * no device memory and keeps no global mutable state: the layout blob is an
+ * immutable, position-independent byte array that may be shared across
+ * streams and calls.
+ *
+ * Errors.  Every function returns SA_OK (0) or a negative status and never
+ * aborts.  Arguments are validated before anything is enqueued, so an error
+ * leaves every output untouched.  A failed kernel launch returns SA_EHIP;
+ * faults during execution surface at the caller's next synchronisation.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sa_status {
+  SA_OK = 0,
+  SA_EINVAL = -1,        /* malformed argument: NULL/misaligned pointer, bad size or pattern */
+  SA_EUNSUPPORTED = -2,  /* well-formed but not implemented: d != 64, dtype, tile shape */
+  SA_ESIZE = -3,         /* a caller buffer is too small (blob or workspace) */
+  SA_EHIP = -4           /* the HIP runtime reported an error at launch */
+};
+
+enum sa_head_kind { SA_LOCAL = 0, SA_STRIDE = 1, SA_SAMEBLOCK = 2, SA_SUMMARY = 3 };
+
+enum sa_dtype { SA_BF16 = 0, SA_FP32 = 1 };
+
+/* Layout flag: a row whose set is empty reads itself (report section 2.2 gives
+ * no rule; the blog post's section 02 forbids empty rows). */
+#define SA_SELF_IF_EMPTY 1u
+
+/* One head's pattern.  c and sub are used by SA_SUMMARY only. */
+typedef struct {
+  int32_t kind;  /* enum sa_head_kind */
+  int32_t l;     /* band width / stride / block length, >= 1 */
+  int32_t c;     /* summary width, 1 <= c <= l */
+  int32_t sub;   /* summary sub-block index, >= 0 (taken mod l / c) */
+} sa_head_pattern;
+
+typedef struct {
+  int64_t n;                     /* sequence length, 1 <= n <= 2^26 */
+  int32_t block_q;               /* query-tile rows: 32, 64 or 128 */
+  int32_t block_k;               /* key-tile columns: 32, 64 or 128 */
+  int32_t num_heads;             /* 1 .. 4096 */
+  const sa_head_pattern* heads;  /* num_heads entries, host memory */
+  uint32_t flags;                /* SA_SELF_IF_EMPTY or 0 */
+} sa_layout_desc;
+
+/* ---------------------------------------------------------------------------
+ * Layout blob.  Built once per (n, tiles, head patterns) and reused by every
+ * forward and backward call (blog post section 09: build the block mask once
+ * for a fixed length and pattern).  All offsets are bytes from the start of
+ * the blob and 64-byte aligned.
+ *
+ * Each distinct head pattern is described in its own "layout space": query
+ * position p in [0, n_pad) holds token qmap[p], key position q holds token
+ * kmap[q] (-1 = padding past n).  The maps are permutations of [0, n):
+ *   SA_LOCAL, SA_SAMEBLOCK: identity.
+ *   SA_STRIDE: residue-class order (the column view of the (n/l) x l grid,
+ *     comparison article "稀疏与局部注意力", section 2): token t*l + r sits at
+ *     position (number of tokens of residues < r) + t, for queries and keys.
+ *   SA_SUMMARY: queries identity; keys are the summary cells in increasing
+ *     order, then the tokens of rows that read only themselves, then every
+ *     other token (keys nobody reads: their dK/dV are zero).
+ * In layout space every query row reads one interval of key positions,
+ * [lo[p], hi[p]] (lo > hi only on padding rows), which is what makes the
+ * per-tile fine mask two comparisons.  Tiles: q-tile i covers positions
+ * [i*block_q, (i+1)*block_q), k-tile j covers [j*block_k, (j+1)*block_k).  A
+ * tile pair is active iff it holds a visible pair, FULL iff every pair in it
+ * is visible.  CSR lists each q-tile's active k-tiles (ascending), CSC each
+ * k-tile's active q-tiles (ascending).
+ * ------------------------------------------------------------------------- */
+
+#define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
+#define SA_BLOB_VERSION 1u
+#define SA_TILE_PARTIAL 0u
+#define SA_TILE_FULL 1u
+
+typedef struct {
+  int32_t kind, l, c, sub;
+  int32_t s;           /* summary: first residue of the sub-block; 0 otherwise */
+  int32_t nnz;         /* active tiles */
+  int64_t pairs;       /* visible (query, key) pairs */
+  int64_t qmap_off;    /* int32[n_pad] */
+  int64_t kmap_off;    /* int32[n_pad] */
+  int64_t lo_off;      /* int32[n_pad] */
+  int64_t hi_off;      /* int32[n_pad] */
+  int64_t count_off;   /* int32[n]: visible keys of token i (token order) */
+  int64_t row_ptr_off; /* int32[nqt + 1] */
+  int64_t col_off;     /* int32[nnz]: k-tile of each CSR entry */
+  int64_t fflag_off;   /* uint8[nnz]: SA_TILE_FULL / SA_TILE_PARTIAL (CSR order) */
+  int64_t col_ptr_off; /* int32[nkt + 1] */
+  int64_t row_off;     /* int32[nnz]: q-tile of each CSC entry */
+  int64_t bflag_off;   /* uint8[nnz]: flags in CSC order */
+} sa_pattern_rec;
+
+typedef struct {
+  uint32_t magic, version;
+  int64_t n;
+  int32_t block_q, block_k;
+  int32_t num_heads, num_patterns;
+  int32_t n_pad;            /* n rounded up to a multiple of max(block_q, block_k) */
+  int32_t nqt, nkt;         /* n_pad / block_q, n_pad / block_k */
+  uint32_t flags;
+  int64_t total_bytes;
+  int64_t head_pattern_off; /* int32[num_heads]: pattern index of each head */
+  int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
+  int64_t fwd_sched_off;    /* int32[2 * fwd_sched_len]: (head, q-tile), heaviest first */
+  int64_t bwd_sched_off;    /* int32[2 * bwd_sched_len]: (head, k-tile), heaviest first */
+  int32_t fwd_sched_len, bwd_sched_len;
+  int64_t pairs_all_heads;  /* sum of pairs over the heads (one batch element) */
+  int64_t tiles_all_heads;  /* sum of active tiles over the heads */
+} sa_blob_header;
+
+/* Build the layout.  With blob == NULL, only *blob_bytes is set (size query).
+ * Otherwise *blob_bytes must hold the blob's capacity (SA_ESIZE if too small)
+ * and is set to the bytes written.  Host-only; needs no GPU. */
+int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_bytes);
+
+/* Check a blob's header and internal offsets (host). */
+int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes);
+
+/* Forward (report sections 3.5 and 3.4): o [B,H,n,d] in dtype, lse [B,H,n]
+ * float32.  scale <= 0 selects 1/sqrt(d).  B == 0 is a valid no-op. */
+int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
+                    const void* q, const void* k, const void* v, void* o, float* lse,
+                    float scale, void* stream);
+
+/* Bytes of device workspace sparse_attn_bwd needs for these sizes. */
+int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
+                              size_t* bytes);
+
+/* Backward by recomputation from LSE (report section 3.4): gradients of
+ * sum(O * dO) with respect to q, k, v, written in dtype.  `o` and `lse` must
+ * be the forward's outputs for the same inputs and scale.  Keys no query
+ * reads in a head get exact zeros.  workspace: ws_bytes >= the size returned
+ * by sparse_attn_bwd_workspace, 16-byte aligned; its contents on entry do not
+ * matter.  Only SA_BF16. */
+int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
+                    const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    void* workspace, size_t ws_bytes, float scale, void* stream);
+
+/* Static description of a status code. */
+const char* sparse_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

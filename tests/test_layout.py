@@ -1,0 +1,284 @@
+"""Host layout builder (C ABI, no GPU): bit-exact against the oracle's token masks.
+
+The reference tiles are derived here, in test code: the documented index
+maps (identity; residue-class order for the stride head; summary cells first
+for the summary head) are rebuilt independently, the oracle's dense token
+mask is permuted by them, and a tile is active iff any entry in it is set and
+FULL iff all are.  CSR, CSC, flags, per-row intervals and per-token counts
+must match bit for bit.
+"""
+
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from oracle import masks as M
+from factorized_block_sparse_amd import binding as bd
+from factorized_block_sparse_amd.binding import HeadPattern, Layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _doc_maps(kind, n, n_pad, l, c=0, sub=0):
+    """Documented layout-space maps (query map, key map), -1 past n."""
+    qmap = -np.ones(n_pad, dtype=np.int64)
+    kmap = -np.ones(n_pad, dtype=np.int64)
+    if kind in ("local", "sameblock"):
+        qmap[:n] = kmap[:n] = np.arange(n)
+    elif kind == "stride":
+        order = sorted(range(n), key=lambda i: (i % l, i // l))
+        qmap[:n] = kmap[:n] = order
+    else:
+        s = M.summary_start(l, c, sub)
+        qmap[:n] = np.arange(n)
+        cells = [j for j in range(n) if s <= j % l <= s + c - 1]
+        empty = [i for i in range(n) if M.row_keys(M.SUMMARY, i, n, l, c, sub, self_if_empty=False).size == 0]
+        rest = [j for j in range(n) if j not in set(cells) | set(empty)]
+        kmap[:n] = cells + empty + rest
+    return qmap, kmap
+
+
+def _ref_tiles(mp, bq, bk):
+    n_pad = mp.shape[0]
+    nqt, nkt = n_pad // bq, n_pad // bk
+    t = mp.reshape(nqt, bq, nkt, bk)
+    active = t.any(axis=(1, 3))
+    full = t.all(axis=(1, 3))
+    row_ptr = np.concatenate([[0], np.cumsum(active.sum(1))]).astype(np.int32)
+    qt_idx, kt_idx = np.nonzero(active)  # row-major: CSR order, ascending k-tiles
+    col = kt_idx.astype(np.int32)
+    fflag = full[qt_idx, kt_idx].astype(np.uint8)
+    col_ptr = np.concatenate([[0], np.cumsum(active.sum(0))]).astype(np.int32)
+    kt2, qt2 = np.nonzero(active.T)
+    return row_ptr, col, fflag, col_ptr, qt2.astype(np.int32), full.T[kt2, qt2].astype(np.uint8)
+
+
+CASES = [
+    # (n, block_q, block_k, heads)
+    (256, 64, 64, [HeadPattern("local", 16), HeadPattern("stride", 16)]),
+    (1024, 32, 32, [HeadPattern("local", 32), HeadPattern("stride", 32)]),
+    (384, 64, 64, [HeadPattern("local", 64), HeadPattern("stride", 64)]),
+    (576, 64, 64, [HeadPattern("local", 24), HeadPattern("stride", 24)]),   # class length 24: straddling tiles
+    (512, 64, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
+                   HeadPattern("summary", 128, 32, 1), HeadPattern("summary", 128, 32, 2),
+                   HeadPattern("summary", 128, 32, 3)]),
+    (512, 128, 64, [HeadPattern("sameblock", 64), HeadPattern("summary", 64, 8, 0),
+                    HeadPattern("summary", 64, 16, 2)]),
+    (300, 64, 32, [HeadPattern("local", 17), HeadPattern("stride", 17), HeadPattern("sameblock", 20),
+                   HeadPattern("summary", 20, 3, 1)]),                          # ragged everywhere
+    (97, 32, 64, [HeadPattern("stride", 10), HeadPattern("summary", 10, 1, 4)]),
+    (1, 32, 32, [HeadPattern("local", 1), HeadPattern("summary", 4, 2, 0)]),
+    (200, 64, 64, [HeadPattern("local", 500), HeadPattern("stride", 500), HeadPattern("summary", 8, 8, 0)]),
+]
+
+
+@pytest.mark.parametrize("n,bq,bk,heads", CASES)
+def test_layout_bit_exact(n, bq, bk, heads):
+    lay = Layout(n, heads, bq, bk)
+    h = lay.header
+    t = max(bq, bk)
+    n_pad = -(-n // t) * t
+    assert (h.magic, h.n, h.n_pad, h.nqt, h.nkt) == (bd.SA_BLOB_MAGIC, n, n_pad, n_pad // bq, n_pad // bk)
+    hp = lay.head_pattern_index()
+    total_pairs = 0
+    for hi_, head in enumerate(heads):
+        arr = lay.pattern_arrays(int(hp[hi_]))
+        rec = lay.pattern_rec(int(hp[hi_]))
+        qmap, kmap = _doc_maps(head.kind, n, n_pad, head.l, head.c, head.sub)
+        np.testing.assert_array_equal(arr["qmap"], qmap)
+        np.testing.assert_array_equal(arr["kmap"], kmap)
+        mask = M.head_mask(n, head.kind, head.l, head.c or None, head.sub)
+        mp = np.zeros((n_pad, n_pad), dtype=bool)
+        mp[:n, :n] = mask[np.ix_(qmap[:n], kmap[:n])]
+        # Every layout row reads exactly one interval [lo, hi].
+        cols = np.arange(n_pad)
+        interval = (cols[None, :] >= arr["lo"][:, None]) & (cols[None, :] <= arr["hi"][:, None])
+        np.testing.assert_array_equal(interval, mp)
+        np.testing.assert_array_equal(arr["count"], mask.sum(1))
+        assert rec.pairs == mask.sum()
+        total_pairs += int(mask.sum())
+        ref = _ref_tiles(mp, bq, bk)
+        for name, r in zip(("row_ptr", "col", "fflag", "col_ptr", "row", "bflag"), ref):
+            np.testing.assert_array_equal(arr[name], r, err_msg=f"{head} {name}")
+        assert rec.nnz == len(ref[1])
+    assert lay.pairs_per_batch() == total_pairs
+
+
+def test_patterns_are_shared_between_equal_heads():
+    heads = [HeadPattern("local", 8), HeadPattern("stride", 8)] * 4 + [HeadPattern("summary", 8, 2, 5)]
+    lay = Layout(64, heads, 32, 32)
+    assert lay.num_patterns == 3
+    assert lay.head_pattern_index().tolist() == [0, 1] * 4 + [2]
+    # sub is taken mod l / c: sub 5 == sub 1
+    assert lay.pattern_rec(2).sub == 1 and lay.pattern_rec(2).s == 4
+
+
+def test_schedules_cover_every_tile_heaviest_first():
+    heads = [HeadPattern("sameblock", 64), HeadPattern("summary", 64, 16, 0)]
+    lay = Layout(1000, heads, 64, 64)
+    h = lay.header
+    fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
+    fwork, bwork = [], []
+    for head, qt in fs:
+        a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
+        fwork.append(a["row_ptr"][qt + 1] - a["row_ptr"][qt])
+    for head, kt in bs:
+        a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
+        bwork.append(a["col_ptr"][kt + 1] - a["col_ptr"][kt])
+    assert all(w > 0 for w in fwork)
+    assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
+    assert sorted(map(tuple, fs.tolist())) == [(hh, q) for hh in range(2) for q in range(h.nqt)
+                                               if q * 64 < 1000]
+    assert sorted(map(tuple, bs.tolist())) == [(hh, k) for hh in range(2) for k in range(h.nkt)
+                                               if k * 64 < 1000]
+
+
+def test_padding_overhead_closed_form_12288():
+    """Computed-tile area per allowed pair for the 12,288-token heads with 64x64 tiles."""
+    lay = Layout(12288, [HeadPattern("local", 128), HeadPattern("stride", 128)], 64, 64)
+    a0, a1 = lay.pattern_arrays(0), lay.pattern_arrays(1)
+    assert lay.pattern_rec(0).pairs == 1576896 and lay.pattern_rec(1).pairs == 595968
+    # local band l=128: q-tile i >= 2 touches k-tiles i-2, i-1, i (the first only partly)
+    assert len(a0["col"]) == 1 + 2 + 3 * (192 - 2)
+    # stride head: 128 classes of 96 tokens; every tile pair touched stays inside a class
+    assert (lay.tiles_per_batch() * 64 * 64) / lay.pairs_per_batch() < 2.0
+
+
+# ----------------------------------------------------------------------------
+# errors, flags, ABI surface
+# ----------------------------------------------------------------------------
+
+def _raw_layout(n, heads, bq=64, bk=64, flags=1):
+    lib = bd.load_library()
+    arr = (bd.CHeadPattern * max(1, len(heads)))(*heads)
+    desc = bd.CLayoutDesc(n, bq, bk, len(heads), arr, flags)
+    size = ctypes.c_size_t(0)
+    return lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)), size.value
+
+
+@pytest.mark.parametrize("n,heads,bq,bk,flags,expect", [
+    (0, [(0, 4, 0, 0)], 64, 64, 1, bd.SA_EINVAL),
+    (-5, [(0, 4, 0, 0)], 64, 64, 1, bd.SA_EINVAL),
+    (64, [(0, 0, 0, 0)], 64, 64, 1, bd.SA_EINVAL),          # l = 0
+    (64, [(3, 8, 0, 0)], 64, 64, 1, bd.SA_EINVAL),          # c = 0
+    (64, [(3, 8, 9, 0)], 64, 64, 1, bd.SA_EINVAL),          # c > l
+    (64, [(3, 8, 2, -1)], 64, 64, 1, bd.SA_EINVAL),         # sub < 0
+    (64, [(7, 8, 0, 0)], 64, 64, 1, bd.SA_EINVAL),          # unknown kind
+    (64, [(0, 8, 0, 0)], 48, 64, 1, bd.SA_EUNSUPPORTED),    # tile not 32/64/128
+    (64, [(0, 8, 0, 0)], 64, 256, 1, bd.SA_EUNSUPPORTED),
+    (64, [(0, 8, 0, 0)], 64, 64, 6, bd.SA_EINVAL),          # unknown flag
+    (64, [(3, 8, 2, 0)], 64, 64, 0, bd.SA_EINVAL),          # empty rows without self-if-empty
+    (64, [], 64, 64, 1, bd.SA_EINVAL),                      # no heads
+    ((1 << 26) + 1, [(0, 8, 0, 0)], 64, 64, 1, bd.SA_EINVAL),
+])
+def test_layout_rejects_bad_descriptors(n, heads, bq, bk, flags, expect):
+    rc, _ = _raw_layout(n, [bd.CHeadPattern(*h) for h in heads], bq, bk, flags)
+    assert rc == expect
+
+
+def test_layout_without_self_if_empty_when_no_row_is_empty():
+    rc, size = _raw_layout(64, [bd.CHeadPattern(3, 8, 8, 0), bd.CHeadPattern(1, 8, 0, 0)], flags=0)
+    assert rc == bd.SA_OK and size > 0
+
+
+def test_layout_buffer_too_small_and_check():
+    lib = bd.load_library()
+    heads = (bd.CHeadPattern * 1)(bd.CHeadPattern(0, 8, 0, 0))
+    desc = bd.CLayoutDesc(128, 64, 64, 1, heads, 1)
+    size = ctypes.c_size_t(0)
+    assert lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)) == 0
+    need = size.value
+    small = np.zeros(need - 64, dtype=np.uint8)
+    size2 = ctypes.c_size_t(small.size)
+    assert lib.sparse_attn_layout(ctypes.byref(desc), small.ctypes.data_as(ctypes.c_void_p),
+                                  ctypes.byref(size2)) == bd.SA_ESIZE
+    assert size2.value == need
+    blob = np.zeros(need, dtype=np.uint8)
+    size3 = ctypes.c_size_t(need)
+    assert lib.sparse_attn_layout(ctypes.byref(desc), blob.ctypes.data_as(ctypes.c_void_p),
+                                  ctypes.byref(size3)) == 0
+    assert lib.sparse_attn_layout_check(blob.ctypes.data, need) == 0
+    assert lib.sparse_attn_layout_check(blob.ctypes.data, need - 1) == bd.SA_ESIZE
+    bad = blob.copy()
+    bad[0] ^= 0xFF
+    assert lib.sparse_attn_layout_check(bad.ctypes.data, need) == bd.SA_EINVAL
+    assert lib.sparse_attn_layout_check(None, need) == bd.SA_EINVAL
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.load_library()
+    with open(os.path.join(ROOT, "include", "sparse_attn.h")) as f:
+        text = f.read()
+    import re
+    declared = set(re.findall(r"\b(sparse_attn_[a-z_]+)\s*\(", text))
+    assert declared == set(bd.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name)
+    assert lib.sparse_attn_strerror(0) == b"success"
+    assert lib.sparse_attn_strerror(-2) == b"unsupported configuration"
+    assert lib.sparse_attn_strerror(99) == b"unknown status"
+
+
+def test_ctypes_structs_match_the_c_header():
+    """Sizes and offsets of the ABI structs, from a C compiler reading the header."""
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "sparse_attn.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu\n", sizeof(sa_head_pattern), sizeof(sa_layout_desc),
+             sizeof(sa_pattern_rec), sizeof(sa_blob_header));
+      printf("%zu %zu %zu\n", offsetof(sa_layout_desc, heads), offsetof(sa_layout_desc, flags),
+             offsetof(sa_blob_header, tiles_all_heads));
+      printf("%zu %zu\n", offsetof(sa_pattern_rec, bflag_off), offsetof(sa_blob_header, bwd_sched_len));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "s.c")
+        exe = os.path.join(d, "s")
+        with open(c, "w") as f:
+            f.write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    got = list(map(int, out))
+    assert got == [ctypes.sizeof(bd.CHeadPattern), ctypes.sizeof(bd.CLayoutDesc),
+                   ctypes.sizeof(bd.CPatternRec), ctypes.sizeof(bd.CBlobHeader),
+                   bd.CLayoutDesc.heads.offset, bd.CLayoutDesc.flags.offset,
+                   bd.CBlobHeader.tiles_all_heads.offset, bd.CPatternRec.bflag_off.offset,
+                   bd.CBlobHeader.bwd_sched_len.offset]
+
+
+def test_fwd_bwd_argument_errors_before_any_launch():
+    """Validation rejects bad arguments before touching the device (runs without a GPU)."""
+    lib = bd.load_library()
+    lay = Layout(128, [HeadPattern("local", 8), HeadPattern("stride", 8)], 64, 64)
+    hb = lay.blob.ctypes.data
+    fake = 1 << 20  # aligned non-null device-looking address; never dereferenced on these paths
+    f = lambda **kw: lib.sparse_attn_fwd(kw.get("blob", hb), kw.get("dev", fake), kw.get("B", 1),
+                                         kw.get("H", 2), kw.get("d", 64), kw.get("dt", 0), fake,
+                                         fake, fake, kw.get("o", fake), fake, kw.get("scale", 0.0), None)
+    assert f(blob=None) == bd.SA_EINVAL
+    assert f(H=3) == bd.SA_EINVAL
+    assert f(B=-1) == bd.SA_EINVAL
+    assert f(d=128) == bd.SA_EUNSUPPORTED
+    assert f(dt=7) == bd.SA_EINVAL
+    assert f(o=None) == bd.SA_EINVAL
+    assert f(o=fake + 2) == bd.SA_EINVAL
+    assert f(dev=fake + 8) == bd.SA_EINVAL
+    assert f(scale=float("nan")) == bd.SA_EINVAL
+    assert f(B=0) == bd.SA_OK  # empty batch: nothing to do
+    size = ctypes.c_size_t(0)
+    assert lib.sparse_attn_bwd_workspace(hb, 2, 2, 64, 0, ctypes.byref(size)) == 0
+    assert size.value == (-(-2 * 2 * 128 * 4 // 256) * 256) + 2 * 2 * 128 * 64 * 4
+    assert lib.sparse_attn_bwd_workspace(hb, 2, 2, 64, 1, ctypes.byref(size)) == bd.SA_EUNSUPPORTED
+    g = lambda **kw: lib.sparse_attn_bwd(hb, fake, kw.get("B", 1), 2, 64, kw.get("dt", 0), fake, fake,
+                                         fake, fake, fake, fake, fake, fake, fake, fake,
+                                         kw.get("ws", 1 << 30), 0.0, None)
+    assert g(ws=16) == bd.SA_ESIZE
+    assert g(dt=1) == bd.SA_EUNSUPPORTED
+    assert g(B=0) == bd.SA_OK
