@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of causal factorized block-sparse attention (forward + backward) on one MI355X.
+
+Metric: useful TFLOP/s of sparse-attention forward + backward at n = 12,288,
+and its fraction of the bf16 MFMA peak.  Useful FLOPs per (batch, head) are
+4 d P (forward) + 8 d P (backward: dV, dP, dQ, dK), P = visible (query, key)
+pairs; the recomputation of the scores in the backward pass is not counted.
+
+One step = forward + backward of both n = 12,288 workloads, on inputs already
+resident in HBM:
+  fixed_n12288    B=2, H=8, l=128, c=32, alternating same-block / summary heads
+  strided_n12288  B=1, H=16, l=128, alternating local / stride heads,
+                  shared period-128 sinusoid in Q and K
+Prints one JSON line.  ``--gpus`` above 1 exits: this build measures one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+D = 64
+DEFAULT_WORKLOADS = ("fixed_n12288", "strided_n12288")
+
+
+# ----------------------------------------------------------------------------
+# algorithmic accounting
+# ----------------------------------------------------------------------------
+
+def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
+    """(flops, bytes) a launch must do at minimum, per kernel."""
+    rows = B * H * n
+    if label == "fwd":
+        return 4 * D * pairs, rows * (4 * D * 2 + 4)            # Q, K, V read, O write, LSE
+    if label == "bwd_main":
+        return 8 * D * pairs, rows * (4 * D * 2 + 8 + 2 * D * 2 + D * 4)  # Q,K,V,dO; LSE,D; dK,dV; dQ acc
+    if label == "bwd_pre":
+        return 2 * D * rows, rows * (2 * D * 2 + 4 + D * 4)     # O, dO read; D write; zero acc
+    if label == "bwd_post":
+        return D * rows, rows * (D * 4 + D * 2)                 # acc read, dQ write
+    raise ValueError(label)
+
+
+def roofline_entry(flops: float, nbytes: float, seconds: float):
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / max(nbytes, 1) >= ridge:
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS}
+    ach = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle (row-gather mode) on a bounded sample, all host cores
+# ----------------------------------------------------------------------------
+
+_CPU = {}
+
+
+def _cpu_task(args):
+    key, rows, deadline = args
+    if time.time() > deadline:
+        return 0, 0.0
+    from oracle import attention as OA
+    q, k, v, do, head, n = _CPU[key]
+    kf = OA.keys_fn_for(head.kind, n, head.l, head.c or None, head.sub)
+    OA.bwd_rows_full(q, k, v, do, kf, rows=rows)
+    fl = 0
+    for i in rows:
+        fl += 12 * D * kf(i).size
+    return len(rows), float(fl)
+
+
+def cpu_baseline(workloads, inputs, seconds: float):
+    """Oracle forward + backward rows for ~`seconds` of wall time on a process pool."""
+    import numpy as np
+    cores = min(os.cpu_count() or 1, 16)
+    tasks = []
+    for w in workloads:
+        inp = inputs[w.name]
+        seen = {}
+        for h, head in enumerate(w.heads):
+            if head in seen:
+                continue
+            seen[head] = h
+            key = (w.name, h)
+            _CPU[key] = tuple(inp[x][0, h].double().numpy() for x in ("q", "k", "v", "do")) + (head, w.n)
+            rng = np.random.default_rng(h + 17)
+            perm = rng.permutation(w.n)
+            for c in range(0, w.n, 8):
+                tasks.append((key, sorted(perm[c:c + 8].tolist())))
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(tasks))
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    ctx = mp.get_context("fork")
+    t0 = time.time()
+    deadline = t0 + seconds
+    rows_done = 0
+    flops = 0.0
+    with ctx.Pool(cores) as pool:
+        for r, f in pool.imap_unordered(_cpu_task, [(tasks[i][0], tasks[i][1], deadline) for i in order],
+                                        chunksize=1):
+            rows_done += r
+            flops += f
+    wall = time.time() - t0
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{rows_done} query rows (random, every distinct head pattern of "
+                       f"{'+'.join(w.name for w in workloads)}, batch 0) through the float64 "
+                       f"row-gather oracle forward+backward in {wall:.1f} s; useful FLOPs 12*d*keys per row"),
+            "seconds": wall}
+
+
+# ----------------------------------------------------------------------------
+# GPU run
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the attention path is single-GPU; see the design notes for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from factorized_block_sparse_amd import binding as bd
+    from factorized_block_sparse_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    names = [s for s in args.workloads.split(",") if s]
+    wls = [W.WORKLOADS[nm] for nm in names]
+    inputs, runs = {}, []
+    for w in wls:
+        lay = bd.Layout(w.n, w.heads, w.block_q, w.block_k)
+        inp = W.workload_inputs(w)
+        inputs[w.name] = inp
+        q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(bd.bwd_workspace_bytes(lay, w.B, w.H), dtype=torch.uint8, device=dev)
+        pairs = lay.pairs_per_batch() * w.B
+        calls = [("fwd", lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse: bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse))]
+        if w.backward:
+            for label, ph in (("bwd_pre", bd.SA_BWD_PREPARE), ("bwd_main", bd.SA_BWD_MAIN),
+                              ("bwd_post", bd.SA_BWD_FINISH)):
+                calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, do=do, ws=ws, grads=grads, ph=ph:
+                              bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads, phases=ph)))
+        useful = (12 if w.backward else 4) * D * pairs
+        tiles = lay.tiles_per_batch() * w.B
+        runs.append(dict(w=w, lay=lay, calls=calls, pairs=pairs, useful=useful,
+                         padding=tiles * w.block_q * w.block_k / pairs))
+
+    flat = [(r["w"], label, fn) for r in runs for (label, fn) in r["calls"]]
+
+    def step(evs=None):
+        for i, (_, _, fn) in enumerate(flat):
+            if evs is not None:
+                evs[i].record()
+            fn()
+        if evs is not None:
+            evs[len(flat)].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(flat) + 1)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    per_call_ms = [sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)) / K for i in range(len(flat))]
+
+    useful = sum(r["useful"] for r in runs)
+    value = useful / (ms_per_step * 1e-3) / 1e12
+
+    # per-workload and per-kernel breakdown
+    per_wl, kernels, idx = {}, [], 0
+    for r in runs:
+        w = r["w"]
+        ms = 0.0
+        for label, _ in r["calls"]:
+            t = per_call_ms[idx]
+            ms += t
+            fl, by = kernel_work(label, w.B, w.H, w.n, r["pairs"])
+            kernels.append(dict(workload=w.name, kernel=label, ms=t, flops=fl, bytes=by))
+            idx += 1
+        tf = r["useful"] / (ms * 1e-3) / 1e12
+        per_wl[w.name] = {"ms": round(ms, 4), "useful_tflops": round(tf, 2),
+                          "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                          "pairs": r["pairs"], "tile_padding_overhead": round(r["padding"], 3)}
+    dom = max(kernels, key=lambda k: k["ms"])
+    roof = roofline_entry(dom["flops"], dom["bytes"], dom["ms"] * 1e-3)
+    roof.update({"traffic": None, "kernel": f"{dom['kernel']} ({dom['workload']})",
+                 "launch_us": round(dom["ms"] * 1e3, 2)})
+    for k in kernels:
+        k["ms"] = round(k["ms"], 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wls, inputs, args.cpu_seconds)
+
+    line = {
+        "metric": "sparse-attn fwd+bwd useful TFLOP/s at n=12288; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "config": {"workload": "+".join(names),
+                   "shapes": {w.name: {"B": w.B, "H": w.H, "n": w.n, "d": w.d,
+                                       "heads": sorted({h.kind for h in w.heads}),
+                                       "tiles": [w.block_q, w.block_k]} for w in wls},
+                   "per_workload": per_wl, "kernels": kernels},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -28,8 +28,10 @@ SA_TILE_PARTIAL, SA_TILE_FULL = 0, 1
 
 EXPORTED = (
     "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd",
-    "sparse_attn_bwd_workspace", "sparse_attn_bwd", "sparse_attn_strerror",
+    "sparse_attn_bwd_workspace", "sparse_attn_bwd", "sparse_attn_bwd_phases",
+    "sparse_attn_strerror",
 )
+SA_BWD_PREPARE, SA_BWD_MAIN, SA_BWD_FINISH, SA_BWD_ALL = 1, 2, 4, 7
 
 
 class CHeadPattern(ctypes.Structure):
@@ -101,6 +103,9 @@ def load_library():
         lib.sparse_attn_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, sz, f32, vp]
         lib.sparse_attn_bwd.restype = i32
+        lib.sparse_attn_bwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, sz, f32, ctypes.c_uint, vp]
+        lib.sparse_attn_bwd_phases.restype = i32
         lib.sparse_attn_strerror.argtypes = [i32]
         lib.sparse_attn_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -270,8 +275,12 @@ def bwd_workspace_bytes(layout: Layout, B: int, H: int, d: int = 64, dtype: int 
 
 
 def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = None,
-                    workspace=None, grads=None):
-    """Backward on the current torch stream: returns (dq, dk, dv)."""
+                    workspace=None, grads=None, phases: int = SA_BWD_ALL):
+    """Backward on the current torch stream: returns (dq, dk, dv).
+
+    ``phases`` selects which of the three launches run (see
+    ``sparse_attn_bwd_phases`` in the C header); the default runs all.
+    """
     import torch
     lib = load_library()
     B, H, n, d, dt = _check_qkv(layout, (q, k, v, o, do), ("q", "k", "v", "o", "do"))
@@ -284,9 +293,13 @@ def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = N
     dq, dk, dv = grads
     blob_dev = layout.device_blob(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.sparse_attn_bwd(layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
-                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
-                             0.0 if scale is None else float(scale), stream)
+    args = (layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+            0.0 if scale is None else float(scale))
+    if phases == SA_BWD_ALL:
+        rc = lib.sparse_attn_bwd(*args, stream)
+    else:
+        rc = lib.sparse_attn_bwd_phases(*args, phases, stream)
     _check(rc, "sparse_attn_bwd")
     return dq, dk, dv

@@ -1,0 +1,112 @@
+// Device-side types and helpers shared by the gfx950 forward and backward
+// kernels: vector types for MFMA operands, lane-layout permutations, and the
+// view of the layout blob.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;  // head dimension handled by these kernels
+
+// ---------------------------------------------------------------------------
+// 32x32 MFMA lane layout (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2f32).
+// A operand: lane L holds row L%32; B operand: lane L holds column L%32; the
+// K slots of lane L belong to half g = L/32.  The result holds column L%32 in
+// lane L and row 8*(r/4) + 4*g + r%4 in register r (16 registers).
+//
+// Loading the A-operand rows through sigma (swap bits 2 and 3 of the row
+// index) makes register r of half g hold logical row kappa(r, g) =
+// 16*(r/8) + 8*g + r%8: registers 0..7 of a half are 8 consecutive rows and
+// registers 8..15 the next group of 16.  That is exactly the K-slot order of
+// a following 32x32x16 MFMA, so a result can feed the next product as a B
+// operand without any data movement.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int sigma32(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+__device__ __forceinline__ int kappa32(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
+__device__ __forceinline__ floatx16 mfma_bf16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma_f32(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane L ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+// Two floats -> two bf16 packed in 32 bits, round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  floatx2 f = {lo, hi};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
+  u32x4 u = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+             pack_bf16x2(p[6], p[7])};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float bf16_to_float(bf16 x) { return float(x); }
+
+// ---------------------------------------------------------------------------
+// Layout blob (device copy): header + per-pattern records, see sparse_attn.h.
+// ---------------------------------------------------------------------------
+struct PatView {
+  const int32_t* qmap;
+  const int32_t* kmap;
+  const int32_t* lo;
+  const int32_t* hi;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const uint8_t* fflag;
+  const int32_t* col_ptr;
+  const int32_t* row;
+  const uint8_t* bflag;
+};
+
+__device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head) {
+  const sa_blob_header* hdr = reinterpret_cast<const sa_blob_header*>(blob);
+  const int32_t* head_pat = reinterpret_cast<const int32_t*>(blob + hdr->head_pattern_off);
+  const int pi = head_pat[head];
+  const sa_pattern_rec* rec =
+      reinterpret_cast<const sa_pattern_rec*>(blob + hdr->pattern_off) + pi;
+  PatView v;
+  v.qmap = reinterpret_cast<const int32_t*>(blob + rec->qmap_off);
+  v.kmap = reinterpret_cast<const int32_t*>(blob + rec->kmap_off);
+  v.lo = reinterpret_cast<const int32_t*>(blob + rec->lo_off);
+  v.hi = reinterpret_cast<const int32_t*>(blob + rec->hi_off);
+  v.row_ptr = reinterpret_cast<const int32_t*>(blob + rec->row_ptr_off);
+  v.col = reinterpret_cast<const int32_t*>(blob + rec->col_off);
+  v.fflag = blob + rec->fflag_off;
+  v.col_ptr = reinterpret_cast<const int32_t*>(blob + rec->col_ptr_off);
+  v.row = reinterpret_cast<const int32_t*>(blob + rec->row_off);
+  v.bflag = blob + rec->bflag_off;
+  return v;
+}
+
+// Host-side copy of the few header fields the launchers need.
+struct HostLayoutInfo {
+  int64_t n;
+  int32_t block_q, block_k, num_heads, n_pad, nqt, nkt;
+  int32_t fwd_sched_len, bwd_sched_len;
+  int64_t fwd_sched_off, bwd_sched_off;
+};
+
+}  // namespace sa

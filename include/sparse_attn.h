@@ -179,6 +179,22 @@ int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, i
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     void* workspace, size_t ws_bytes, float scale, void* stream);
 
+/* The backward as three separately launchable phases, for callers that
+ * interleave other work between them or time them one by one:
+ *   SA_BWD_PREPARE  D_i = dO_i . O_i and a zeroed float32 dQ accumulator
+ *                   (both in the workspace);
+ *   SA_BWD_MAIN     the block-sparse recomputation kernel (dK, dV written,
+ *                   dQ accumulated in the workspace);
+ *   SA_BWD_FINISH   dQ = scale * accumulator, written in dtype.
+ * Phases must run in this order on one stream with the same arguments and
+ * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL). */
+enum { SA_BWD_PREPARE = 1, SA_BWD_MAIN = 2, SA_BWD_FINISH = 4, SA_BWD_ALL = 7 };
+int sparse_attn_bwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
+                           int dtype, const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                           void* workspace, size_t ws_bytes, float scale, unsigned phases,
+                           void* stream);
+
 /* Static description of a status code. */
 const char* sparse_attn_strerror(int status);
 

@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases compare every element (several tiles, ragged tails, every head
+kind, all tile shapes).  Full-size workloads compare sampled rows and keys
+that the oracle computes one by one, plus invariants that hold at any size.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from factorized_block_sparse_amd import binding as bd
+from factorized_block_sparse_amd import workloads as W
+from factorized_block_sparse_amd.binding import HeadPattern, Layout
+from oracle import attention as OA
+from oracle import masks as OM
+from tests.parity_util import (BF16_MAX_ABS, BF16_REL_RMS, FP32_MAX_ABS, LSE_ABS, assert_close,
+                               oracle_dense_head, run_gpu, to64)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, B, n, block_q, block_k, heads
+    ("strided_tiles64", 2, 512, 64, 64, [HeadPattern("local", 32), HeadPattern("stride", 32)]),
+    ("strided_straddle", 1, 576, 64, 64, [HeadPattern("local", 24), HeadPattern("stride", 24)]),
+    ("fixed_c32", 1, 768, 64, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
+                                   HeadPattern("summary", 128, 32, 1), HeadPattern("summary", 128, 32, 3)]),
+    ("fixed_c8_q128", 1, 640, 128, 64, [HeadPattern("sameblock", 64), HeadPattern("summary", 64, 8, 0),
+                                        HeadPattern("summary", 64, 16, 2)]),
+    ("ragged_all_kinds", 2, 333, 64, 32, [HeadPattern("local", 17), HeadPattern("stride", 17),
+                                          HeadPattern("sameblock", 20), HeadPattern("summary", 20, 3, 1)]),
+    ("ragged_q32_k64", 1, 301, 32, 64, [HeadPattern("stride", 10), HeadPattern("summary", 10, 1, 4)]),
+    ("tiles32", 1, 256, 32, 32, [HeadPattern("local", 16), HeadPattern("stride", 16)]),
+    ("degenerate", 1, 130, 64, 64, [HeadPattern("local", 1000), HeadPattern("stride", 1000),
+                                    HeadPattern("summary", 8, 8, 0), HeadPattern("stride", 1)]),
+    ("single_row", 1, 1, 64, 64, [HeadPattern("local", 4), HeadPattern("summary", 4, 2, 0)]),
+]
+
+
+def _check_dense(layout, heads, B, n, inp, backward=True, fp32=False):
+    out = run_gpu(layout, inp, backward)
+    q, k, v, do = (to64(inp[x]) for x in ("q", "k", "v", "do"))
+    for b in range(B):
+        for h, head in enumerate(heads):
+            o, lse, g = oracle_dense_head(head, n, q[b, h], k[b, h], v[b, h], do[b, h] if backward else None)
+            tag = f"b{b} h{h} {head}"
+            if fp32:
+                assert_close(f"O {tag}", out["o"][b, h], o, FP32_MAX_ABS)
+                assert_close(f"LSE {tag}", out["lse"][b, h], lse, 1e-5)
+                continue
+            assert_close(f"O {tag}", out["o"][b, h], o, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"LSE {tag}", out["lse"][b, h], lse, LSE_ABS)
+            if backward:
+                for nm, ref in zip(("dq", "dk", "dv"), g):
+                    assert_close(f"{nm} {tag}", out[nm][b, h], ref, BF16_MAX_ABS, BF16_REL_RMS)
+    return out
+
+
+@pytest.mark.parametrize("name,B,n,bq,bk,heads", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_every_element(name, B, n, bq, bk, heads):
+    lay = Layout(n, heads, bq, bk)
+    inp = W.make_inputs(B, len(heads), n, 64, seed=zlib.crc32(name.encode()) % 10000)
+    _check_dense(lay, heads, B, n, inp)
+
+
+def test_fp32_forward_small_ragged():
+    heads = [HeadPattern("local", 9), HeadPattern("stride", 9), HeadPattern("summary", 9, 3, 0)]
+    lay = Layout(200, heads, 32, 32)
+    inp = W.make_inputs(1, 3, 200, 64, seed=5, dtype="fp32")
+    _check_dense(lay, heads, 1, 200, inp, backward=False, fp32=True)
+
+
+def test_workload_strided_n1024_fp32_full():
+    """Strided pattern, forward only, float32, 32x32 tiles: every element."""
+    w = W.WORKLOADS["strided_n1024_fp32"]
+    lay = Layout(w.n, w.heads, w.block_q, w.block_k)
+    _check_dense(lay, w.heads, w.B, w.n, W.workload_inputs(w), backward=False, fp32=True)
+
+
+def test_workload_strided_n3072_full():
+    """Strided pattern n = 3072, B = 4, H = 8: every element of every (b, h)."""
+    w = W.WORKLOADS["strided_n3072"]
+    lay = Layout(w.n, w.heads, w.block_q, w.block_k)
+    _check_dense(lay, w.heads, w.B, w.n, W.workload_inputs(w))
+
+
+def test_empty_batch_is_a_no_op():
+    heads = [HeadPattern("local", 8), HeadPattern("stride", 8)]
+    lay = Layout(64, heads, 64, 64)
+    q = torch.zeros((0, 2, 64, 64), dtype=torch.bfloat16, device="cuda:0")
+    o, lse = bd.sparse_attn_fwd(lay, q, q, q)
+    dq, dk, dv = bd.sparse_attn_bwd(lay, q, q, q, o, lse, q)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0
+
+
+def test_repeat_calls_are_deterministic_forward_and_close_backward():
+    """Forward is bitwise reproducible; backward (float atomics for dQ) within rounding."""
+    heads = [HeadPattern("sameblock", 64), HeadPattern("summary", 64, 16, 0)]
+    lay = Layout(1024, heads, 64, 64)
+    inp = W.make_inputs(1, 2, 1024, 64, seed=77)
+    a = run_gpu(lay, inp, True)
+    b = run_gpu(lay, inp, True)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+    assert np.array_equal(a["dk"], b["dk"]) and np.array_equal(a["dv"], b["dv"])
+    assert np.max(np.abs(a["dq"] - b["dq"])) <= 1e-2
+
+
+def test_masked_value_perturbation_on_gpu():
+    """Blog post on sliding windows, section 10: a masked key's value cannot reach a row."""
+    heads = [HeadPattern("local", 8), HeadPattern("stride", 8)]
+    n = 256
+    lay = Layout(n, heads, 64, 64)
+    inp = W.make_inputs(1, 2, n, 64, seed=3)
+    base = run_gpu(lay, inp, False)
+    j = 100
+    inp2 = dict(inp)
+    v2 = inp["v"].clone()
+    v2[:, :, j] += 10000
+    inp2["v"] = v2
+    pert = run_gpu(lay, inp2, False)
+    for h, head in enumerate(heads):
+        blind = ~OM.head_mask(n, head.kind, head.l)[:, j]
+        assert np.array_equal(base["o"][0, h][blind], pert["o"][0, h][blind])
+        assert not np.allclose(base["o"][0, h][~blind], pert["o"][0, h][~blind])
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads: sampled rows / keys + invariants
+# ----------------------------------------------------------------------------
+
+def _sample_rows(n, l, rng, extra=6):
+    base = {0, 1, l - 1, l, 2 * l + 3, n // 2, n - 2, n - 1, 95, 96, 127, 128}
+    base |= set(rng.integers(0, n, extra).tolist())
+    return sorted(r for r in base if 0 <= r < n)
+
+
+@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "strided_n65536"])
+def test_workload_full_size_sampled(wname):
+    w = W.WORKLOADS[wname]
+    lay = Layout(w.n, w.heads, w.block_q, w.block_k)
+    inp = W.workload_inputs(w)
+    out = run_gpu(lay, inp, True)
+    rng = np.random.default_rng(2024)
+    q, k, v, do = (to64(inp[x]) for x in ("q", "k", "v", "do"))
+    heads_to_check = range(w.H) if w.H <= 4 else sorted({0, 1, 2, 3, w.H - 2, w.H - 1})
+    for b in range(w.B):
+        for h in (heads_to_check if b == 0 else (0, 1)):
+            head = w.heads[h]
+            kf = OA.keys_fn_for(head.kind, w.n, head.l, head.c or None, head.sub)
+            rf = OA.rows_seeing_fn_for(head.kind, w.n, head.l, head.c or None, head.sub)
+            rows = _sample_rows(w.n, head.l, rng)
+            o, lse = OA.fwd_rows(q[b, h], k[b, h], v[b, h], kf, rows)
+            tag = f"{wname} b{b} h{h} {head.kind}"
+            assert_close(f"O {tag}", out["o"][b, h][rows], o, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"LSE {tag}", out["lse"][b, h][rows], lse, LSE_ABS)
+            dq = OA.bwd_rows_dq(q[b, h], k[b, h], v[b, h], do[b, h], kf, rows)
+            assert_close(f"dQ {tag}", out["dq"][b, h][rows], dq, BF16_MAX_ABS, BF16_REL_RMS)
+            if head.kind == "summary":
+                s = OM.summary_start(head.l, head.c, head.sub)
+                keys = [s, s + head.c - 1, w.n - head.l + s]         # summary cells
+                keys += [max(0, s - 1)] if s > 0 else []             # a self-if-empty key
+                cand = [head.l + (s + head.c) % head.l, w.n - 1, w.n - head.l + (s - 1) % head.l]
+                dead = [j for j in cand if rf(j).size == 0]
+                assert dead
+            else:
+                keys = sorted({0, 1, head.l, w.n // 3, w.n - 1, int(rng.integers(0, w.n))})
+                dead = []
+            dk, dv = OA.bwd_keys_dkdv(q[b, h], k[b, h], v[b, h], do[b, h], kf, rf, keys)
+            assert_close(f"dK {tag}", out["dk"][b, h][keys], dk, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"dV {tag}", out["dv"][b, h][keys], dv, BF16_MAX_ABS, BF16_REL_RMS)
+            for j in dead:
+                assert (out["dk"][b, h][j] == 0).all() and (out["dv"][b, h][j] == 0).all()
+    # Invariants at full size for every (b, h): sum_j dK_j = 0, sum_j dV_j = sum_i dO_i.
+    for b in range(w.B):
+        for h in range(w.H):
+            sk = out["dk"][b, h].sum(0)
+            scale_k = np.abs(out["dk"][b, h]).sum(0).max() + 1e-30
+            assert np.max(np.abs(sk)) <= 2e-2 * scale_k + 1e-3, (b, h)
+            sv = out["dv"][b, h].sum(0)
+            ref = do[b, h].sum(0)
+            assert np.max(np.abs(sv - ref)) <= 1e-2 * np.abs(out["dv"][b, h]).sum(0).max() + 1e-2, (b, h)
+    assert np.isfinite(out["o"]).all() and np.isfinite(out["dq"]).all()
