@@ -91,17 +91,15 @@ def cpu_baseline(workloads, inputs, seconds: float):
     tasks = []
     for w in workloads:
         inp = inputs[w.name]
-        seen = {}
-        for h, head in enumerate(w.heads):
-            if head in seen:
-                continue
-            seen[head] = h
-            key = (w.name, h)
-            _CPU[key] = tuple(inp[x][0, h].double().numpy() for x in ("q", "k", "v", "do")) + (head, w.n)
-            rng = np.random.default_rng(h + 17)
-            perm = rng.permutation(w.n)
-            for c in range(0, w.n, 8):
-                tasks.append((key, sorted(perm[c:c + 8].tolist())))
+        for b in range(w.B):
+            for h, head in enumerate(w.heads):
+                key = (w.name, b, h)
+                _CPU[key] = tuple(inp[x][b, h].double().numpy() for x in ("q", "k", "v", "do")) + (head, w.n)
+                rng = np.random.default_rng(1000 * b + h + 17)
+                perm = rng.permutation(w.n)
+                for c in range(0, w.n, 8):
+                    tasks.append((key, sorted(perm[c:c + 8].tolist())))
+    total_rows = sum(len(t[1]) for t in tasks)
     rng = np.random.default_rng(0)
     order = rng.permutation(len(tasks))
     os.environ.setdefault("OMP_NUM_THREADS", "1")
@@ -117,9 +115,10 @@ def cpu_baseline(workloads, inputs, seconds: float):
             flops += f
     wall = time.time() - t0
     return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{rows_done} query rows (random, every distinct head pattern of "
-                       f"{'+'.join(w.name for w in workloads)}, batch 0) through the float64 "
-                       f"row-gather oracle forward+backward in {wall:.1f} s; useful FLOPs 12*d*keys per row"),
+            "sample": (f"{rows_done} of the {total_rows} query rows of {'+'.join(w.name for w in workloads)} "
+                       f"(random order over every batch element and head) through the float64 row-gather "
+                       f"oracle forward+backward in {wall:.1f} s of wall time (deadline {seconds:.0f} s); "
+                       f"useful FLOPs 12*d*keys per row"),
             "seconds": wall}
 
 

@@ -368,16 +368,16 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   const bool bq_ok = li.block_q == 32 || li.block_q == 64 || li.block_q == 128;
   const bool bk_ok = li.block_k == 32 || li.block_k == 64;
   if (!bq_ok || !bk_ok) return SA_EUNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      !aligned16(workspace))
-    return SA_EINVAL;
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
   const int64_t rows = int64_t(B) * H * li.n;
+  if (B == 0) return SA_OK;  // empty batch: pointers may be NULL
   if (ws_bytes < workspace_bytes(rows)) return SA_ESIZE;
-  if (B == 0) return SA_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(workspace))
+    return SA_EINVAL;
   const int64_t grid = int64_t(li.bwd_sched_len) * B;
   if (grid > INT32_MAX || rows * 8 / 256 + 1 > INT32_MAX) return SA_EUNSUPPORTED;
 

@@ -378,12 +378,12 @@ extern "C" int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int 
   LaunchInfo li;
   int rc = validate_common(blob_host, blob_dev, B, H, d, dtype, &li);
   if (rc != SA_OK) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return SA_EINVAL;
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
-  if (B == 0 || li.fwd_sched_len == 0) return SA_OK;
+  if (B == 0 || li.fwd_sched_len == 0) return SA_OK;  // empty batch: pointers may be NULL
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return SA_EINVAL;
   const int64_t grid = int64_t(li.fwd_sched_len) * B;
   if (grid > INT32_MAX) return SA_EUNSUPPORTED;
 

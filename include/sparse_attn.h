@@ -159,7 +159,8 @@ int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_byte
 int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes);
 
 /* Forward (report sections 3.5 and 3.4): o [B,H,n,d] in dtype, lse [B,H,n]
- * float32.  scale <= 0 selects 1/sqrt(d).  B == 0 is a valid no-op. */
+ * float32.  scale <= 0 selects 1/sqrt(d).  B == 0 is a valid no-op (the
+ * tensor pointers may then be NULL). */
 int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
                     const void* q, const void* k, const void* v, void* o, float* lse,
                     float scale, void* stream);

@@ -1,8 +1,11 @@
 """Shared helpers of the GPU parity tests: run the HIP path, run the oracle, compare.
 
-Tolerances (bf16 data, fp32 accumulation): max |err| <= 2e-2 and relative
-RMS (||x - ref||_2 / ||ref||_2) <= 1e-2 on O, dQ, dK, dV; LSE to 1e-3
-absolute (it is float32 from exactly the same bf16 inputs).  float32 data:
+Tolerances (bf16 data, fp32 accumulation): relative RMS
+(||x - ref||_2 / ||ref||_2) <= 1e-2 and, element by element,
+|x - ref| <= 2e-2 + ulp_bf16(ref) / 2 on O, dQ, dK, dV.  The half-ULP term is
+the rounding of the bf16 output itself: at |ref| >= 8 it alone exceeds 2e-2,
+so the 2e-2 bar is read as the error beyond the output's own rounding.  LSE
+(float32 from exactly the same bf16 inputs) to 1e-3 absolute.  float32 data:
 max |err| <= 1e-4 on O.
 """
 
@@ -29,11 +32,23 @@ def rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref)) / (den if den > 0 else 1.0)
 
 
+def half_ulp_bf16(ref: np.ndarray) -> np.ndarray:
+    """Half the spacing of bfloat16 numbers at |ref| (8 significant bits)."""
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - 7)
+
+
 def assert_close(name: str, got: np.ndarray, ref: np.ndarray, max_abs: float,
-                 rel: float | None = None):
-    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+                 rel: float | None = None, bf16_output: bool = False):
     assert np.isfinite(got).all(), f"{name}: non-finite values"
-    assert err <= max_abs, f"{name}: max |err| {err:.3e} > {max_abs:.1e}"
+    if not got.size:
+        return
+    diff = np.abs(got - ref)
+    bound = max_abs + (half_ulp_bf16(ref) if bf16_output else 0.0)
+    worst = int(np.argmax(diff - bound))
+    assert (diff <= bound).all(), (f"{name}: |err| {diff.flat[worst]:.3e} > bound "
+                                   f"{np.broadcast_to(bound, diff.shape).flat[worst]:.3e} "
+                                   f"at ref {ref.flat[worst]:+.4f} (max |err| {diff.max():.3e})")
     if rel is not None:
         r = rel_rms(got, ref)
         assert r <= rel, f"{name}: rel RMS {r:.3e} > {rel:.1e}"

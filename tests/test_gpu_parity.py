@@ -50,11 +50,11 @@ def _check_dense(layout, heads, B, n, inp, backward=True, fp32=False):
                 assert_close(f"O {tag}", out["o"][b, h], o, FP32_MAX_ABS)
                 assert_close(f"LSE {tag}", out["lse"][b, h], lse, 1e-5)
                 continue
-            assert_close(f"O {tag}", out["o"][b, h], o, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"O {tag}", out["o"][b, h], o, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
             assert_close(f"LSE {tag}", out["lse"][b, h], lse, LSE_ABS)
             if backward:
                 for nm, ref in zip(("dq", "dk", "dv"), g):
-                    assert_close(f"{nm} {tag}", out[nm][b, h], ref, BF16_MAX_ABS, BF16_REL_RMS)
+                    assert_close(f"{nm} {tag}", out[nm][b, h], ref, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
     return out
 
 
@@ -154,10 +154,10 @@ def test_workload_full_size_sampled(wname):
             rows = _sample_rows(w.n, head.l, rng)
             o, lse = OA.fwd_rows(q[b, h], k[b, h], v[b, h], kf, rows)
             tag = f"{wname} b{b} h{h} {head.kind}"
-            assert_close(f"O {tag}", out["o"][b, h][rows], o, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"O {tag}", out["o"][b, h][rows], o, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
             assert_close(f"LSE {tag}", out["lse"][b, h][rows], lse, LSE_ABS)
             dq = OA.bwd_rows_dq(q[b, h], k[b, h], v[b, h], do[b, h], kf, rows)
-            assert_close(f"dQ {tag}", out["dq"][b, h][rows], dq, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"dQ {tag}", out["dq"][b, h][rows], dq, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
             if head.kind == "summary":
                 s = OM.summary_start(head.l, head.c, head.sub)
                 keys = [s, s + head.c - 1, w.n - head.l + s]         # summary cells
@@ -169,8 +169,8 @@ def test_workload_full_size_sampled(wname):
                 keys = sorted({0, 1, head.l, w.n // 3, w.n - 1, int(rng.integers(0, w.n))})
                 dead = []
             dk, dv = OA.bwd_keys_dkdv(q[b, h], k[b, h], v[b, h], do[b, h], kf, rf, keys)
-            assert_close(f"dK {tag}", out["dk"][b, h][keys], dk, BF16_MAX_ABS, BF16_REL_RMS)
-            assert_close(f"dV {tag}", out["dv"][b, h][keys], dv, BF16_MAX_ABS, BF16_REL_RMS)
+            assert_close(f"dK {tag}", out["dk"][b, h][keys], dk, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
+            assert_close(f"dV {tag}", out["dv"][b, h][keys], dv, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
             for j in dead:
                 assert (out["dk"][b, h][j] == 0).all() and (out["dv"][b, h][j] == 0).all()
     # Invariants at full size for every (b, h): sum_j dK_j = 0, sum_j dV_j = sum_i dO_i.
