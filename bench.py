@@ -43,12 +43,16 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
     rows = B * H * n
     if label == "fwd":
         return 4 * D * pairs, rows * (4 * D * 2 + 4)            # Q, K, V read, O write, LSE
-    if label == "bwd_main":
-        return 8 * D * pairs, rows * (4 * D * 2 + 8 + 2 * D * 2 + D * 4)  # Q,K,V,dO; LSE,D; dK,dV; dQ acc
-    if label == "bwd_pre":
-        return 2 * D * rows, rows * (2 * D * 2 + 4 + D * 4)     # O, dO read; D write; zero acc
-    if label == "bwd_post":
-        return D * rows, rows * (D * 4 + D * 2)                 # acc read, dQ write
+    # The backward's 8 d useful FLOPs per pair are split between its kernels as
+    # the products each one forms for its own outputs: dQ = dS K (2 d) in the
+    # query-tile pass; dV = P^T dO, dP = dO V^T and dK = dS^T Q (6 d) in the
+    # key-tile pass.  Score recomputation is not counted.
+    if label == "bwd_dq":
+        return 2 * D * pairs, rows * (5 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
+    if label == "bwd_dkdv":
+        return 6 * D * pairs, rows * (6 * D * 2 + 8)             # Q,K,V,dO read, dK,dV write; LSE, D
+    if label == "bwd_reduce":
+        return 0, 0
     raise ValueError(label)
 
 
@@ -161,8 +165,8 @@ def main():
         pairs = lay.pairs_per_batch() * w.B
         calls = [("fwd", lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse: bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse))]
         if w.backward:
-            for label, ph in (("bwd_pre", bd.SA_BWD_PREPARE), ("bwd_main", bd.SA_BWD_MAIN),
-                              ("bwd_post", bd.SA_BWD_FINISH)):
+            for label, ph in (("bwd_dq", bd.SA_BWD_DQ), ("bwd_dkdv", bd.SA_BWD_DKDV),
+                              ("bwd_reduce", bd.SA_BWD_REDUCE)):
                 calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, do=do, ws=ws, grads=grads, ph=ph:
                               bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads, phases=ph)))
         useful = (12 if w.backward else 4) * D * pairs

@@ -31,7 +31,7 @@ EXPORTED = (
     "sparse_attn_bwd_workspace", "sparse_attn_bwd", "sparse_attn_bwd_phases",
     "sparse_attn_strerror",
 )
-SA_BWD_PREPARE, SA_BWD_MAIN, SA_BWD_FINISH, SA_BWD_ALL = 1, 2, 4, 7
+SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_REDUCE, SA_BWD_ALL = 1, 2, 4, 7
 
 
 class CHeadPattern(ctypes.Structure):
@@ -63,6 +63,8 @@ class CBlobHeader(ctypes.Structure):
                 ("head_pattern_off", ctypes.c_int64), ("pattern_off", ctypes.c_int64),
                 ("fwd_sched_off", ctypes.c_int64), ("bwd_sched_off", ctypes.c_int64),
                 ("fwd_sched_len", ctypes.c_int32), ("bwd_sched_len", ctypes.c_int32),
+                ("red_sched_off", ctypes.c_int64), ("red_sched_len", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32),
                 ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64)]
 
 
@@ -201,7 +203,12 @@ class Layout:
         return self._arr(self.header.fwd_sched_off, 2 * self.header.fwd_sched_len, np.int32).reshape(-1, 2)
 
     def bwd_schedule(self) -> np.ndarray:
-        return self._arr(self.header.bwd_sched_off, 2 * self.header.bwd_sched_len, np.int32).reshape(-1, 2)
+        """Rows (head, k-tile, first CSC entry, end CSC entry, partial slot or -1)."""
+        return self._arr(self.header.bwd_sched_off, 5 * self.header.bwd_sched_len, np.int32).reshape(-1, 5)
+
+    def reduce_schedule(self) -> np.ndarray:
+        """Rows (head, k-tile, first partial slot, chunks) of the split key tiles."""
+        return self._arr(self.header.red_sched_off, 4 * self.header.red_sched_len, np.int32).reshape(-1, 4)
 
     def pairs_per_batch(self) -> int:
         """Visible (query, key) pairs summed over the heads of one batch element."""

@@ -7,21 +7,20 @@
 //     dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale sum_j dS_ij k_j,
 //     dK_j = scale sum_i dS_ij q_i.
 //
-// Three launches on the caller's stream:
-//   bwd_pre   D_i = rowsum(dO_i * O_i) (float32) and a zeroed float32 dQ
-//             accumulator, one pass over the query rows;
-//   bwd_main  one workgroup per key tile (block_k keys of one (batch, head)),
-//             walking that tile's CSC list of query tiles.  Each wave owns
-//             32 keys and keeps K, V (as MFMA operands) and its dK, dV
-//             accumulators in registers.  Per query tile: Q, Q^T, dO, dO^T,
-//             LSE and D are staged in LDS; S = Q K^T and dP = dO V^T on the
-//             MFMA units; P and dS in registers; dV^T += dO^T P and
-//             dK^T += Q^T dS on the MFMA units; dS goes through LDS so that
-//             dQ = dS K (all keys of the tile) is formed per query block and
-//             added to the float32 accumulator with atomics.  The tile's dK,
-//             dV rows are written once at the end (exact zeros for keys no
-//             query reads);
-//   bwd_post  dQ = scale * accumulator, cast to the output type.
+// Three launches on the caller's stream, none with atomics (deterministic):
+//   bwd_dq    one workgroup per query tile (the forward's tiling): D_i for its
+//             rows (kept in the workspace for the next pass), then a walk of
+//             the tile's CSR key tiles: S^T = K Q^T and dP^T = V dO^T on the
+//             MFMA units, P and dS in registers, dQ^T += K^T dS^T on the MFMA
+//             units; dQ written once;
+//   bwd_dkdv  one workgroup per key tile (or per chunk of a long key tile's
+//             CSC list): each wave owns 32 keys with K, V held as MFMA
+//             operands and dK, dV accumulated in registers; per query tile,
+//             Q, Q^T, dO, dO^T, LSE and D are staged in LDS; S = Q K^T and
+//             dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.  Unsplit
+//             tiles write dK, dV (exact zeros for keys no query reads); chunks
+//             of split tiles write float32 partial sums to the workspace;
+//   bwd_reduce sums the chunks of each split key tile in chunk order.
 
 #include <math.h>
 
@@ -33,8 +32,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
   const uint8_t* blob;
-  const int32_t* sched;  // (head, k-tile) pairs
-  int32_t B, H, n;
+  const int32_t* qsched;    // (head, q-tile) pairs: the forward schedule
+  const int32_t* ksched;    // (head, k-tile, e0, e1, slot)
+  const int32_t* rsched;    // (head, k-tile, slot0, chunks)
+  int32_t B, H, n, num_slots;
   const bf16* q;
   const bf16* k;
   const bf16* v;
@@ -44,100 +45,199 @@ struct BwdParams {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* dsum;    // D, [B, H, n]
-  float* dq_acc;  // [B, H, n, 64]
+  float* dsum;     // D, [B, H, n]
+  float* partial;  // [B, num_slots, 2, BK, 64]
   float scale;
   float scale_log2;
-  int64_t rows;  // B * H * n
 };
 
 // --------------------------------------------------------------------------
-// D = rowsum(dO * O); zero the dQ accumulator.  8 threads per row.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = t >> 3;
-  const int part = int(t & 7);
-  float acc = 0.f;
-  if (row < p.rows) {
-    const bf16x8 a = reinterpret_cast<const bf16x8*>(p.o + row * kD)[part];
-    const bf16x8 b = reinterpret_cast<const bf16x8*>(p.dout + row * kD)[part];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc += float(a[j]) * float(b[j]);
-    floatx4* z = reinterpret_cast<floatx4*>(p.dq_acc + row * kD) + 2 * part;
-    z[0] = floatx4{};
-    z[1] = floatx4{};
-  }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
-  if (row < p.rows && part == 0) p.dsum[row] = acc;
-}
-
-// --------------------------------------------------------------------------
-// dQ = scale * accumulator -> bf16.  One thread per 8 features.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_post_kernel(BwdParams p) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= p.rows * 8) return;
-  const floatx4* src = reinterpret_cast<const floatx4*>(p.dq_acc) + 2 * t;
-  const floatx4 a = src[0], b = src[1];
-  float tmp[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) tmp[j] *= p.scale;
-  reinterpret_cast<bf16x8*>(p.dq)[t] = pack_bf16x8(tmp);
-}
-
-// --------------------------------------------------------------------------
-// Main kernel.  BK = 32 * NW keys per workgroup; query tiles of BQ rows are
-// processed in steps of QS = min(BQ, 64) rows.
+// dQ pass: one workgroup per query tile, BQ = 32 * NW rows, key tiles of BK.
 // --------------------------------------------------------------------------
 template <int BQ, int BK>
-__global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
-  constexpr int NW = BK / 32;
+__global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
-  constexpr int QS = BQ < 64 ? BQ : 64;  // query rows per step
-  constexpr int NSTEP = BQ / QS;
-  constexpr int NQB = QS / 32;          // 32-row query blocks per step
-  constexpr int RS = kD + 8;            // row stride of Q / dO in LDS
-  constexpr int TS = QS + 8;            // row stride of Q^T / dO^T in LDS
-  constexpr int DSS = BK + 8;           // row stride of dS in LDS
-  constexpr int KTS = BK + 8;           // row stride of K^T in LDS
-  constexpr int CPT = QS * 8 / NT;      // 16-byte chunks per thread and tensor per step
-  static_assert(CPT >= 1 && (QS * 8) % NT == 0, "tile/wave mismatch");
-  constexpr int NUNITS = NQB * 2;       // dQ work units: (query block, feature block)
-
-  __shared__ __attribute__((aligned(16))) bf16 sq[QS * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sqt[kD * TS];
-  __shared__ __attribute__((aligned(16))) bf16 sdo[QS * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sdot[kD * TS];
-  __shared__ __attribute__((aligned(16))) bf16 sds[QS * DSS];
-  __shared__ __attribute__((aligned(16))) bf16 skt[kD * KTS];
-  __shared__ __attribute__((aligned(16))) float slse[QS];
-  __shared__ __attribute__((aligned(16))) float sdd[QS];
-  __shared__ __attribute__((aligned(16))) int32_t slo[QS];
-  __shared__ __attribute__((aligned(16))) int32_t shi[QS];
-  __shared__ __attribute__((aligned(16))) int32_t stok[2][QS];  // by step parity: read after restaging
+  constexpr int NKB = BK / 32;
+  constexpr int KS = kD + 8;   // row stride of K, V in LDS
+  constexpr int TS = BK + 8;   // row stride of K^T in LDS
+  constexpr int CPT = BK * 8 / NT;
+  static_assert(CPT >= 1 && (BK * 8) % NT == 0, "tile/wave mismatch");
+  __shared__ __attribute__((aligned(16))) bf16 ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) bf16 vs[BK * KS];
+  __shared__ __attribute__((aligned(16))) bf16 kts[kD * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.x % p.B;
   const int item = blockIdx.x / p.B;
-  const int head = p.sched[2 * item], kt = p.sched[2 * item + 1];
+  const int head = p.qsched[2 * item], qt = p.qsched[2 * item + 1];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
-  // This lane's key (column of S): position kt*BK + 32w + l32.
+  const int prow = qt * BQ + w * 32 + l32;
+  const int tok = pv.qmap[prow];
+  const int lo = pv.lo[prow], hi = pv.hi[prow];
+
+  bf16x8 qf[4], dof[4];
+  float dsum = 0.f, lse2 = 0.f;
+  if (tok >= 0) {
+    const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(p.q + (base + tok) * kD);
+    const bf16x8* dsrc = reinterpret_cast<const bf16x8*>(p.dout + (base + tok) * kD);
+    const bf16x8* osrc = reinterpret_cast<const bf16x8*>(p.o + (base + tok) * kD);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qf[c] = qsrc[2 * c + g];
+      dof[c] = dsrc[2 * c + g];
+      const bf16x8 oo = osrc[2 * c + g];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum += float(oo[j]) * float(dof[c][j]);
+    }
+    lse2 = p.lse[base + tok] * kLog2e;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qf[c] = bf16x8{};
+      dof[c] = bf16x8{};
+    }
+  }
+  dsum += other_half(dsum);
+  if (tok >= 0 && g == 0) p.dsum[base + tok] = dsum;
+
+  const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
+  u32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
+      const int tk = pv.kmap[kt * BK + j];
+      if (tk >= 0) {
+        kreg[i] = reinterpret_cast<const u32x4*>(p.k + (base + tk) * kD)[cc];
+        vreg[i] = reinterpret_cast<const u32x4*>(p.v + (base + tk) * kD)[cc];
+      } else {
+        kreg[i] = u32x4{0u, 0u, 0u, 0u};
+        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
+      *reinterpret_cast<u32x4*>(&ks[j * KS + cc * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&vs[j * KS + cc * 8]) = vreg[i];
+      const bf16x8 kk = __builtin_bit_cast(bf16x8, kreg[i]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) kts[(cc * 8 + t) * TS + j] = kk[t];
+    }
+  };
+
+  floatx16 dqa[2];
+  dqa[0] = dqa[1] = floatx16{};
+  const float c2 = p.scale_log2;
+  if (e0 < e1) gload(pv.col[e0]);
+  for (int it = e0; it < e1; ++it) {
+    const int kt = pv.col[it];
+    const bool full = pv.fflag[it] == SA_TILE_FULL;
+    lstore();
+    __syncthreads();
+    if (it + 1 < e1) gload(pv.col[it + 1]);
+    const int k0 = kt * BK;
+    const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
+    if (__any(mine)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        floatx16 s = floatx16{}, dp = floatx16{};
+        const int roff = (32 * kb + sigma32(l32)) * KS + 8 * g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[roff + 16 * c]), qf[c], s);
+          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[roff + 16 * c]), dof[c], dp);
+        }
+        // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(s[r] * c2 - lse2);
+          if (!full) {
+            const int kp = k0 + 32 * kb + kappa32(r, g);
+            pr = (kp >= lo && kp <= hi) ? pr : 0.f;
+          }
+          ds[r] = pr * (dp[r] - dsum);
+        }
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const bf16x8 db = pack_bf16x8(&ds[8 * h8]);
+#pragma unroll
+          for (int fb = 0; fb < 2; ++fb) {
+            const bf16* arow = &kts[(32 * fb + sigma32(l32)) * TS + 32 * kb + 16 * h8 + 8 * g];
+            dqa[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(arow), db, dqa[fb]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (tok >= 0) {
+    bf16* row = p.dq + (base + tok) * kD;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = dqa[fb][8 * h8 + j] * p.scale;
+        *reinterpret_cast<bf16x8*>(row + 32 * fb + 16 * h8 + 8 * g) = pack_bf16x8(tmp);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
+// dK/dV pass: one workgroup per (key tile, chunk of its CSC list).
+// BK = 32 * NW keys; query tiles of BQ rows are processed in steps of
+// QS = min(BQ, 64) rows.
+// --------------------------------------------------------------------------
+template <int BQ, int BK>
+__global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = BK / 32;
+  constexpr int NT = NW * 64;
+  constexpr int QS = BQ < 64 ? BQ : 64;
+  constexpr int NSTEP = BQ / QS;
+  constexpr int NQB = QS / 32;
+  constexpr int RS = kD + 8;  // row stride of Q / dO in LDS
+  constexpr int TS = QS + 8;  // row stride of Q^T / dO^T in LDS
+  constexpr int CPT = QS * 8 / NT;
+  static_assert(CPT >= 1 && (QS * 8) % NT == 0, "tile/wave mismatch");
+
+  __shared__ __attribute__((aligned(16))) bf16 sq[QS * RS];
+  __shared__ __attribute__((aligned(16))) bf16 sqt[kD * TS];
+  __shared__ __attribute__((aligned(16))) bf16 sdo[QS * RS];
+  __shared__ __attribute__((aligned(16))) bf16 sdot[kD * TS];
+  __shared__ __attribute__((aligned(16))) float slse[QS];
+  __shared__ __attribute__((aligned(16))) float sdd[QS];
+  __shared__ __attribute__((aligned(16))) int32_t slo[QS];
+  __shared__ __attribute__((aligned(16))) int32_t shi[QS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.x % p.B;
+  const int item = blockIdx.x / p.B;
+  const int32_t* it5 = p.ksched + 5 * item;
+  const int head = it5[0], kt = it5[1], c0 = it5[2], c1 = it5[3], slot = it5[4];
+  const PatView pv = pattern_of_head(p.blob, head);
+  const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
+
   const int kpos = kt * BK + 32 * w + l32;
   const int ktok = pv.kmap[kpos];
   bf16x8 kq[4], vq[4];
   if (ktok >= 0) {
-    const bf16x8* ks = reinterpret_cast<const bf16x8*>(p.k + (base + ktok) * kD);
-    const bf16x8* vs = reinterpret_cast<const bf16x8*>(p.v + (base + ktok) * kD);
+    const bf16x8* ksrc = reinterpret_cast<const bf16x8*>(p.k + (base + ktok) * kD);
+    const bf16x8* vsrc = reinterpret_cast<const bf16x8*>(p.v + (base + ktok) * kD);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kq[c] = ks[2 * c + g];
-      vq[c] = vs[2 * c + g];
+      kq[c] = ksrc[2 * c + g];
+      vq[c] = vsrc[2 * c + g];
     }
   } else {
 #pragma unroll
@@ -146,22 +246,15 @@ __global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
       vq[c] = bf16x8{};
     }
   }
-  // K^T for the dQ product: skt[feature][key].
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) skt[(16 * c + 8 * g + j) * KTS + 32 * w + l32] = kq[c][j];
 
   floatx16 dva[2], dka[2];
   dva[0] = dva[1] = dka[0] = dka[1] = floatx16{};
-
-  const int c0 = pv.col_ptr[kt], c1 = pv.col_ptr[kt + 1];
   const int nsteps = (c1 - c0) * NSTEP;
   const float c2 = p.scale_log2;
 
   u32x4 qreg[CPT], doreg[CPT];
   float lse_r = 0.f, dd_r = 0.f;
-  int lo_r = 1, hi_r = 0, tok_r = -1;
+  int lo_r = 1, hi_r = 0;
   auto gload = [&](int step) {
     const int e = c0 + step / NSTEP;
     const int r0 = pv.row[e] * BQ + (step % NSTEP) * QS;
@@ -179,19 +272,14 @@ __global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
     }
     if (tid < QS) {
       const int r = r0 + tid;
-      tok_r = pv.qmap[r];
+      const int tk = pv.qmap[r];
       lo_r = pv.lo[r];
       hi_r = pv.hi[r];
-      if (tok_r >= 0) {
-        lse_r = p.lse[base + tok_r] * kLog2e;
-        dd_r = p.dsum[base + tok_r];
-      } else {
-        lse_r = 0.f;
-        dd_r = 0.f;
-      }
+      lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : 0.f;
+      dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
     }
   };
-  auto lstore = [&](int parity) {
+  auto lstore = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT, j = c >> 3, cc = c & 7;
@@ -210,33 +298,27 @@ __global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
       sdd[tid] = dd_r;
       slo[tid] = lo_r;
       shi[tid] = hi_r;
-      stok[parity][tid] = tok_r;
     }
   };
 
-  if (nsteps > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
+  if (nsteps > 0) gload(0);
   for (int step = 0; step < nsteps; ++step) {
     const int e = c0 + step / NSTEP;
     const bool full = pv.bflag[e] == SA_TILE_FULL;
+    lstore();
+    __syncthreads();
     if (step + 1 < nsteps) gload(step + 1);
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
       floatx16 s = floatx16{}, dp = floatx16{};
-      const bf16* qrow = &sq[(32 * qb + sigma32(l32)) * RS + 8 * g];
-      const bf16* dorow = &sdo[(32 * qb + sigma32(l32)) * RS + 8 * g];
+      const int roff = (32 * qb + sigma32(l32)) * RS + 8 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * c), kq[c], s);
-        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(dorow + 16 * c), vq[c], dp);
+        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[roff + 16 * c]), kq[c], s);
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[roff + 16 * c]), vq[c], dp);
       }
-      // Register r of half g holds query 32*qb + kappa(r, g), key = lane.
+      // Register r of half g: query 32*qb + kappa(r, g); lane = key.
       float pr[16], ds[16];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
@@ -248,19 +330,17 @@ __global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * h8 + j;
-          const float lse2 = j < 4 ? la[j] : lb[j - 4];
+          const float l2 = j < 4 ? la[j] : lb[j - 4];
           const float dd = j < 4 ? da[j] : db[j - 4];
-          float pv_ = fast_exp2(s[r] * c2 - lse2);
+          float pp = fast_exp2(s[r] * c2 - l2);
           if (!full) {
             const int qi = qloc + j;
-            const bool vis = kpos >= slo[qi] && kpos <= shi[qi];
-            pv_ = vis ? pv_ : 0.f;
+            pp = (kpos >= slo[qi] && kpos <= shi[qi]) ? pp : 0.f;
           }
-          pr[r] = pv_;
-          ds[r] = pv_ * (dp[r] - dd);
+          pr[r] = pp;
+          ds[r] = pp * (dp[r] - dd);
         }
       }
-      // dV^T += dO^T P ;  dK^T += Q^T dS   (K slots = 16 queries per MFMA).
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const bf16x8 pb = pack_bf16x8(&pr[8 * h8]);
@@ -272,53 +352,83 @@ __global__ __launch_bounds__(BK * 2) void bwd_main_kernel(BwdParams p) {
           dka[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sqt[trow]), sb, dka[fb]);
         }
       }
-      // dS -> LDS as [query][key] (bf16) for the dQ product.
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sds[(32 * qb + kappa32(r, g)) * DSS + 32 * w + l32] = bf16(ds[r]);
-    }
-    __syncthreads();
-    if (step + 1 < nsteps) lstore((step + 1) & 1);  // staging buffers are free; dS, K^T untouched
-
-    // dQ[query block][feature block] = dS K over all BK keys of the tile.
-    for (int u = w; u < NUNITS; u += NW) {
-      const int qb = u >> 1, fb = u & 1;
-      floatx16 acc = floatx16{};
-      const bf16* arow = &sds[(32 * qb + sigma32(l32)) * DSS + 8 * g];
-      const bf16* brow = &skt[(32 * fb + l32) * KTS + 8 * g];
-#pragma unroll
-      for (int c = 0; c < BK / 16; ++c)
-        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(arow + 16 * c),
-                        *reinterpret_cast<const bf16x8*>(brow + 16 * c), acc);
-      // Register r of half g: query 32*qb + kappa(r, g), feature 32*fb + lane.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tq = stok[step & 1][32 * qb + kappa32(r, g)];
-        if (tq >= 0) unsafeAtomicAdd(p.dq_acc + (base + tq) * kD + 32 * fb + l32, acc[r]);
-      }
     }
     __syncthreads();
   }
 
-  // dK, dV rows of this wave's 32 keys; register r of half g = feature
-  // 32*fb + kappa(r, g), lane = key.
-  if (ktok >= 0) {
-    bf16* dkrow = p.dk + (base + ktok) * kD;
-    bf16* dvrow = p.dv + (base + ktok) * kD;
+  // Register r of half g: feature 32*fb + kappa(r, g); lane = key.
+  if (slot < 0) {
+    if (ktok >= 0) {
+      bf16* dkrow = p.dk + (base + ktok) * kD;
+      bf16* dvrow = p.dv + (base + ktok) * kD;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          float tk[8], tv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            tk[j] = dka[fb][8 * h8 + j] * p.scale;
+            tv[j] = dva[fb][8 * h8 + j];
+          }
+          const int f0 = 32 * fb + 16 * h8 + 8 * g;
+          *reinterpret_cast<bf16x8*>(dkrow + f0) = pack_bf16x8(tk);
+          *reinterpret_cast<bf16x8*>(dvrow + f0) = pack_bf16x8(tv);
+        }
+    }
+  } else {
+    float* part = p.partial + (size_t(b) * p.num_slots + slot) * 2 * BK * kD;
+    float* pk = part + (32 * w + l32) * kD;
+    float* pvv = part + BK * kD + (32 * w + l32) * kD;
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
-        float tk[8], tv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          tk[j] = dka[fb][8 * h8 + j] * p.scale;
-          tv[j] = dva[fb][8 * h8 + j];
-        }
         const int f0 = 32 * fb + 16 * h8 + 8 * g;
-        *reinterpret_cast<bf16x8*>(dkrow + f0) = pack_bf16x8(tk);
-        *reinterpret_cast<bf16x8*>(dvrow + f0) = pack_bf16x8(tv);
+        floatx4 k0, k1, v0, v1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          k0[j] = dka[fb][8 * h8 + j] * p.scale;
+          k1[j] = dka[fb][8 * h8 + 4 + j] * p.scale;
+          v0[j] = dva[fb][8 * h8 + j];
+          v1[j] = dva[fb][8 * h8 + 4 + j];
+        }
+        *reinterpret_cast<floatx4*>(pk + f0) = k0;
+        *reinterpret_cast<floatx4*>(pk + f0 + 4) = k1;
+        *reinterpret_cast<floatx4*>(pvv + f0) = v0;
+        *reinterpret_cast<floatx4*>(pvv + f0 + 4) = v1;
       }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Sum the chunk partials of each split key tile (chunk order) -> dK, dV.
+// --------------------------------------------------------------------------
+template <int BK>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
+  const int b = blockIdx.x % p.B;
+  const int item = blockIdx.x / p.B;
+  const int32_t* it4 = p.rsched + 4 * item;
+  const int head = it4[0], kt = it4[1], slot0 = it4[2], chunks = it4[3];
+  const PatView pv = pattern_of_head(p.blob, head);
+  const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
+  constexpr int PER = 2 * BK * kD;  // floats per slot
+  const float* part0 = p.partial + (size_t(b) * p.num_slots + slot0) * PER;
+  for (int idx = threadIdx.x * 8; idx < PER; idx += 256 * 8) {
+    floatx4 a = floatx4{}, c = floatx4{};
+    for (int ch = 0; ch < chunks; ++ch) {
+      const floatx4* src = reinterpret_cast<const floatx4*>(part0 + size_t(ch) * PER + idx);
+      a += src[0];
+      c += src[1];
+    }
+    const int t = idx / (BK * kD);  // 0: dK, 1: dV
+    const int key = (idx / kD) % BK;
+    const int f = idx % kD;
+    const int tok = pv.kmap[kt * BK + key];
+    if (tok < 0) continue;
+    float tmp[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    bf16* dst = (t == 0 ? p.dk : p.dv) + (base + tok) * kD + f;
+    *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
   }
 }
 
@@ -333,8 +443,9 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t workspace_bytes(int64_t rows) {
-  return round256(size_t(rows) * sizeof(float)) + size_t(rows) * sa::kD * sizeof(float);
+size_t workspace_bytes(int64_t rows, int B, int32_t num_slots, int32_t bk) {
+  return round256(size_t(rows) * sizeof(float)) +
+         size_t(B) * size_t(num_slots) * 2 * size_t(bk) * sa::kD * sizeof(float);
 }
 
 }  // namespace
@@ -349,7 +460,7 @@ extern "C" int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, in
   if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
   if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
   if (d != 64 || dtype != SA_BF16) return SA_EUNSUPPORTED;
-  *bytes = workspace_bytes(int64_t(B) * H * h.n);
+  *bytes = workspace_bytes(int64_t(B) * H * h.n, B, h.num_slots, h.block_k);
   return SA_OK;
 }
 
@@ -365,28 +476,34 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   int rc = validate_common(blob_host, blob_dev, B, H, d, dtype, &li);
   if (rc != SA_OK) return rc;
   if (dtype != SA_BF16) return SA_EUNSUPPORTED;
-  const bool bq_ok = li.block_q == 32 || li.block_q == 64 || li.block_q == 128;
-  const bool bk_ok = li.block_k == 32 || li.block_k == 64;
-  if (!bq_ok || !bk_ok) return SA_EUNSUPPORTED;
+  const int bq = li.block_q, bk = li.block_k;
+  if (!(bq == 32 || bq == 64 || bq == 128) || !(bk == 32 || bk == 64)) return SA_EUNSUPPORTED;
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
+  sa_blob_header h;
+  memcpy(&h, blob_host, sizeof(h));
   const int64_t rows = int64_t(B) * H * li.n;
   if (B == 0) return SA_OK;  // empty batch: pointers may be NULL
-  if (ws_bytes < workspace_bytes(rows)) return SA_ESIZE;
+  if (ws_bytes < workspace_bytes(rows, B, h.num_slots, bk)) return SA_ESIZE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return SA_EINVAL;
-  const int64_t grid = int64_t(li.bwd_sched_len) * B;
-  if (grid > INT32_MAX || rows * 8 / 256 + 1 > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t gq = int64_t(li.fwd_sched_len) * B;
+  const int64_t gk = int64_t(li.bwd_sched_len) * B;
+  const int64_t gr = int64_t(h.red_sched_len) * B;
+  if (gq > INT32_MAX || gk > INT32_MAX || gr > INT32_MAX) return SA_EUNSUPPORTED;
 
   BwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
-  prm.sched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
+  prm.qsched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
+  prm.ksched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
+  prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
   prm.B = B;
   prm.H = H;
   prm.n = int32_t(li.n);
+  prm.num_slots = h.num_slots;
   prm.q = static_cast<const bf16*>(q);
   prm.k = static_cast<const bf16*>(k);
   prm.v = static_cast<const bf16*>(v);
@@ -397,26 +514,36 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.dk = static_cast<bf16*>(dk);
   prm.dv = static_cast<bf16*>(dv);
   prm.dsum = static_cast<float*>(workspace);
-  prm.dq_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                        ((size_t(rows) * sizeof(float) + 255) & ~size_t(255)));
+  prm.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         round256(size_t(rows) * sizeof(float)));
   prm.scale = sc;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
-  prm.rows = rows;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 pre_grid{unsigned((rows * 8 + 255) / 256), 1u, 1u};
-  if (phases & SA_BWD_PREPARE) hipLaunchKernelGGL(bwd_pre_kernel, pre_grid, dim3(256), 0, st, prm);
-  const dim3 grd{unsigned(grid), 1u, 1u};
-  const int bq = li.block_q, bk = li.block_k;
-  if (!(phases & SA_BWD_MAIN) || grid == 0) {
-    // nothing to launch for the main phase
-  } else if (bq == 32 && bk == 32) hipLaunchKernelGGL((bwd_main_kernel<32, 32>), grd, dim3(64), 0, st, prm);
-  else if (bq == 64 && bk == 32) hipLaunchKernelGGL((bwd_main_kernel<64, 32>), grd, dim3(64), 0, st, prm);
-  else if (bq == 128 && bk == 32) hipLaunchKernelGGL((bwd_main_kernel<128, 32>), grd, dim3(64), 0, st, prm);
-  else if (bq == 32 && bk == 64) hipLaunchKernelGGL((bwd_main_kernel<32, 64>), grd, dim3(128), 0, st, prm);
-  else if (bq == 64 && bk == 64) hipLaunchKernelGGL((bwd_main_kernel<64, 64>), grd, dim3(128), 0, st, prm);
-  else if (bq == 128 && bk == 64) hipLaunchKernelGGL((bwd_main_kernel<128, 64>), grd, dim3(128), 0, st, prm);
-  if (phases & SA_BWD_FINISH) hipLaunchKernelGGL(bwd_post_kernel, pre_grid, dim3(256), 0, st, prm);
+
+#define SA_LAUNCH(kern, grid, threads) \
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(threads), 0, st, prm)
+  if ((phases & SA_BWD_DQ) && gq > 0) {
+    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_dq_kernel<32, 32>), gq, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_dq_kernel<32, 64>), gq, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_dq_kernel<64, 32>), gq, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_dq_kernel<64, 64>), gq, 128);
+    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_dq_kernel<128, 32>), gq, 256);
+    else SA_LAUNCH((bwd_dq_kernel<128, 64>), gq, 256);
+  }
+  if ((phases & SA_BWD_DKDV) && gk > 0) {
+    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<32, 32>), gk, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<64, 32>), gk, 64);
+    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<128, 32>), gk, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_dkdv_kernel<32, 64>), gk, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_dkdv_kernel<64, 64>), gk, 128);
+    else SA_LAUNCH((bwd_dkdv_kernel<128, 64>), gk, 128);
+  }
+  if ((phases & SA_BWD_REDUCE) && gr > 0) {
+    if (bk == 32) SA_LAUNCH((bwd_reduce_kernel<32>), gr, 256);
+    else SA_LAUNCH((bwd_reduce_kernel<64>), gr, 256);
+  }
+#undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;
 }
 

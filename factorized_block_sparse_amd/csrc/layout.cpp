@@ -222,16 +222,24 @@ struct Writer {
 
 struct SchedItem {
   int32_t head, tile, work;
+  int32_t e0 = 0, e1 = 0, slot = -1;
 };
 
-std::vector<int32_t> sorted_schedule(std::vector<SchedItem> items) {
+// Heaviest first; ties keep (head, tile) order.  `fields` = 2 (head, tile) or
+// 5 (head, tile, e0, e1, slot).
+std::vector<int32_t> sorted_schedule(std::vector<SchedItem> items, int fields) {
   std::stable_sort(items.begin(), items.end(),
                    [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
   std::vector<int32_t> out;
-  out.reserve(items.size() * 2);
+  out.reserve(items.size() * fields);
   for (const auto& it : items) {
     out.push_back(it.head);
     out.push_back(it.tile);
+    if (fields == 5) {
+      out.push_back(it.e0);
+      out.push_back(it.e1);
+      out.push_back(it.slot);
+    }
   }
   return out;
 }
@@ -271,6 +279,9 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   }
 
   std::vector<SchedItem> fwd_items, bwd_items;
+  std::vector<int32_t> red_sched;  // (head, k-tile, first slot, chunks)
+  int32_t num_slots = 0;
+  const int32_t cap = std::max<int32_t>(1, SA_SPLIT_ROWS / bq);  // q-tiles per dK/dV chunk
   int64_t pairs_all = 0, tiles_all = 0;
   for (int32_t h = 0; h < desc->num_heads; ++h) {
     const Pattern& P = pats[head_pat[h]];
@@ -282,11 +293,30 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     }
     for (int32_t kt = 0; kt < nkt; ++kt) {
       if (kt * bk >= n) continue;  // all padding keys
-      bwd_items.push_back({h, kt, P.col_ptr[kt + 1] - P.col_ptr[kt] + 1});
+      const int32_t c0 = P.col_ptr[kt], c1 = P.col_ptr[kt + 1], len = c1 - c0;
+      if (len <= cap) {
+        SchedItem it{h, kt, len + 1};
+        it.e0 = c0;
+        it.e1 = c1;
+        bwd_items.push_back(it);
+        continue;
+      }
+      // Split into `chunks` nearly equal runs of CSC entries, one partial slot each.
+      const int32_t chunks = (len + cap - 1) / cap;
+      red_sched.insert(red_sched.end(), {h, kt, num_slots, chunks});
+      for (int32_t c = 0; c < chunks; ++c) {
+        SchedItem it{h, kt, 0};
+        it.e0 = c0 + int32_t(int64_t(len) * c / chunks);
+        it.e1 = c0 + int32_t(int64_t(len) * (c + 1) / chunks);
+        it.work = it.e1 - it.e0 + 1;
+        it.slot = num_slots + c;
+        bwd_items.push_back(it);
+      }
+      num_slots += chunks;
     }
   }
-  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
-  const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
+  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items, 2);
+  const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items, 5);
 
   // Two passes: size, then write.
   for (int pass = 0; pass < 2; ++pass) {
@@ -299,6 +329,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.head_pattern_off = w.put(head_pat);
     hdr.fwd_sched_off = w.put(fwd_sched);
     hdr.bwd_sched_off = w.put(bwd_sched);
+    hdr.red_sched_off = w.put(red_sched);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
       sa_pattern_rec& r = recs[i];
@@ -349,6 +380,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.pattern_off = rec_at;
     hdr.fwd_sched_len = int32_t(fwd_items.size());
     hdr.bwd_sched_len = int32_t(bwd_items.size());
+    hdr.red_sched_len = int32_t(red_sched.size() / 4);
+    hdr.num_slots = num_slots;
     hdr.pairs_all_heads = pairs_all;
     hdr.tiles_all_heads = tiles_all;
     std::memcpy(blob + hdr_at, &hdr, sizeof(hdr));
@@ -391,7 +424,8 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
   if (!in_blob(h.head_pattern_off, 4 * int64_t(h.num_heads), total) ||
       !in_blob(h.pattern_off, int64_t(sizeof(sa_pattern_rec)) * h.num_patterns, total) ||
       !in_blob(h.fwd_sched_off, 8 * int64_t(h.fwd_sched_len), total) ||
-      !in_blob(h.bwd_sched_off, 8 * int64_t(h.bwd_sched_len), total))
+      !in_blob(h.bwd_sched_off, 20 * int64_t(h.bwd_sched_len), total) ||
+      !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0)
     return SA_EINVAL;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

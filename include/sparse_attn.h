@@ -110,7 +110,11 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 1u
+#define SA_BLOB_VERSION 2u
+/* Key tiles read by more than this many query rows are split into chunks for
+ * the dK/dV pass (each chunk a workgroup); their partial sums are reduced in a
+ * fixed order. */
+#define SA_SPLIT_ROWS 1536
 #define SA_TILE_PARTIAL 0u
 #define SA_TILE_FULL 1u
 
@@ -144,8 +148,12 @@ typedef struct {
   int64_t head_pattern_off; /* int32[num_heads]: pattern index of each head */
   int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
   int64_t fwd_sched_off;    /* int32[2 * fwd_sched_len]: (head, q-tile), heaviest first */
-  int64_t bwd_sched_off;    /* int32[2 * bwd_sched_len]: (head, k-tile), heaviest first */
+  int64_t bwd_sched_off;    /* int32[5 * bwd_sched_len]: (head, k-tile, first CSC entry,
+                               end CSC entry, partial slot or -1), heaviest first */
   int32_t fwd_sched_len, bwd_sched_len;
+  int64_t red_sched_off;    /* int32[4 * red_sched_len]: (head, k-tile, first slot, chunks) */
+  int32_t red_sched_len;
+  int32_t num_slots;        /* partial slots per batch element */
   int64_t pairs_all_heads;  /* sum of pairs over the heads (one batch element) */
   int64_t tiles_all_heads;  /* sum of active tiles over the heads */
 } sa_blob_header;
@@ -182,14 +190,15 @@ int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, i
 
 /* The backward as three separately launchable phases, for callers that
  * interleave other work between them or time them one by one:
- *   SA_BWD_PREPARE  D_i = dO_i . O_i and a zeroed float32 dQ accumulator
- *                   (both in the workspace);
- *   SA_BWD_MAIN     the block-sparse recomputation kernel (dK, dV written,
- *                   dQ accumulated in the workspace);
- *   SA_BWD_FINISH   dQ = scale * accumulator, written in dtype.
+ *   SA_BWD_DQ      per query tile: D_i = dO_i . O_i (kept in the workspace)
+ *                  and dQ, written in dtype;
+ *   SA_BWD_DKDV    per key tile (long tiles in chunks): dK, dV written in
+ *                  dtype, or float32 partial sums of split tiles (workspace);
+ *   SA_BWD_REDUCE  sums the partials of split key tiles in a fixed order.
  * Phases must run in this order on one stream with the same arguments and
- * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL). */
-enum { SA_BWD_PREPARE = 1, SA_BWD_MAIN = 2, SA_BWD_FINISH = 4, SA_BWD_ALL = 7 };
+ * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL).
+ * Every phase is deterministic (no atomics). */
+enum { SA_BWD_DQ = 1, SA_BWD_DKDV = 2, SA_BWD_REDUCE = 4, SA_BWD_ALL = 7 };
 int sparse_attn_bwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
                            int dtype, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dO, void* dq, void* dk, void* dv,

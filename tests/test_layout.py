@@ -126,15 +126,48 @@ def test_schedules_cover_every_tile_heaviest_first():
     for head, qt in fs:
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
         fwork.append(a["row_ptr"][qt + 1] - a["row_ptr"][qt])
-    for head, kt in bs:
-        a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
-        bwork.append(a["col_ptr"][kt + 1] - a["col_ptr"][kt])
+    for head, kt, e0, e1, slot in bs:
+        bwork.append(e1 - e0)
     assert all(w > 0 for w in fwork)
     assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
     assert sorted(map(tuple, fs.tolist())) == [(hh, q) for hh in range(2) for q in range(h.nqt)
                                                if q * 64 < 1000]
-    assert sorted(map(tuple, bs.tolist())) == [(hh, k) for hh in range(2) for k in range(h.nkt)
-                                               if k * 64 < 1000]
+    assert sorted({(int(r[0]), int(r[1])) for r in bs}) == [(hh, k) for hh in range(2)
+                                                           for k in range(h.nkt) if k * 64 < 1000]
+
+
+@pytest.mark.parametrize("n,bq,bk,heads", [
+    (12288, 64, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
+                     HeadPattern("summary", 128, 32, 3)]),
+    (5000, 32, 32, [HeadPattern("summary", 64, 4, 1), HeadPattern("local", 3000)]),
+    (3072, 64, 64, [HeadPattern("local", 64), HeadPattern("stride", 64)]),
+])
+def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
+    """Each key tile's CSC list is covered exactly once, in chunks of at most the split cap."""
+    lay = Layout(n, heads, bq, bk)
+    h = lay.header
+    cap = max(1, 1536 // bq)
+    bs, rs = lay.bwd_schedule(), lay.reduce_schedule()
+    slots = sorted(int(r[4]) for r in bs if r[4] >= 0)
+    assert slots == list(range(h.num_slots))
+    red = {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in rs}
+    for head in range(len(heads)):
+        a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
+        for kt in range(h.nkt):
+            if kt * bk >= n:
+                continue
+            rows = sorted((int(r[2]), int(r[3]), int(r[4])) for r in bs if r[0] == head and r[1] == kt)
+            c0, c1 = a["col_ptr"][kt], a["col_ptr"][kt + 1]
+            assert rows[0][0] == c0 and rows[-1][1] == c1
+            assert all(x[1] == y[0] for x, y in zip(rows, rows[1:]))
+            assert all(e1 - e0 <= cap for e0, e1, _ in rows)
+            if c1 - c0 <= cap:
+                assert rows == [(c0, c1, -1)] and (head, kt) not in red
+            else:
+                s0, nch = red[(head, kt)]
+                assert [r[2] for r in rows] == list(range(s0, s0 + nch))
+    if n == 12288:
+        assert h.red_sched_len > 0 and h.num_slots > h.red_sched_len
 
 
 def test_padding_overhead_closed_form_12288():
@@ -274,7 +307,8 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert f(B=0) == bd.SA_OK  # empty batch: nothing to do
     size = ctypes.c_size_t(0)
     assert lib.sparse_attn_bwd_workspace(hb, 2, 2, 64, 0, ctypes.byref(size)) == 0
-    assert size.value == (-(-2 * 2 * 128 * 4 // 256) * 256) + 2 * 2 * 128 * 64 * 4
+    assert lay.header.num_slots == 0
+    assert size.value == -(-2 * 2 * 128 * 4 // 256) * 256  # D only: no split key tiles
     assert lib.sparse_attn_bwd_workspace(hb, 2, 2, 64, 1, ctypes.byref(size)) == bd.SA_EUNSUPPORTED
     g = lambda **kw: lib.sparse_attn_bwd(hb, fake, kw.get("B", 1), 2, 64, kw.get("dt", 0), fake, fake,
                                          fake, fake, fake, fake, fake, fake, fake, fake,
