@@ -29,6 +29,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescales and the
+    # epilogues touch them with VALU code, which AGPRs would force through
+    # copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

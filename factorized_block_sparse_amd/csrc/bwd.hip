@@ -16,13 +16,17 @@
 //   bwd_dkdv  one workgroup per key tile (or per chunk of a long key tile's
 //             CSC list): each wave owns 32 keys with K, V held as MFMA
 //             operands and dK, dV accumulated in registers; per query tile,
-//             Q, Q^T, dO, dO^T, LSE and D are staged in LDS; S = Q K^T and
-//             dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.  Unsplit
+//             Q, dO (row-major), LSE and D are staged in LDS; S = Q K^T and
+//             dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T
+//             through transposing LDS reads).  Unsplit
 //             tiles write dK, dV (exact zeros for keys no query reads); chunks
 //             of split tiles write float32 partial sums to the workspace;
 //   bwd_reduce sums the chunks of each split key tile in chunk order.
 
+#include <limits.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.hpp"
 
@@ -55,17 +59,15 @@ struct BwdParams {
 // dQ pass: one workgroup per query tile, BQ = 32 * NW rows, key tiles of BK.
 // --------------------------------------------------------------------------
 template <int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BQ * 2, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
   constexpr int KS = kD + 8;   // row stride of K, V in LDS
-  constexpr int TS = BK + 8;   // row stride of K^T in LDS
   constexpr int CPT = BK * 8 / NT;
   static_assert(CPT >= 1 && (BK * 8) % NT == 0, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) bf16 vs[BK * KS];
-  __shared__ __attribute__((aligned(16))) bf16 kts[kD * TS];
+  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * KS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -120,48 +122,52 @@ __global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      *reinterpret_cast<u32x4*>(&ks[j * KS + cc * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&vs[j * KS + cc * 8]) = vreg[i];
-      const bf16x8 kk = __builtin_bit_cast(bf16x8, kreg[i]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) kts[(cc * 8 + t) * TS + j] = kk[t];
+      *reinterpret_cast<u32x4*>(&ks[buf][j * KS + cc * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&vs[buf][j * KS + cc * 8]) = vreg[i];
     }
   };
 
   floatx16 dqa[2];
   dqa[0] = dqa[1] = floatx16{};
   const float c2 = p.scale_log2;
-  if (e0 < e1) gload(pv.col[e0]);
+  if (e0 < e1) {
+    gload(pv.col[e0]);
+    lstore(0);
+  }
+  __syncthreads();
   for (int it = e0; it < e1; ++it) {
+    const int buf = (it - e0) & 1;
     const int kt = pv.col[it];
     const bool full = pv.fflag[it] == SA_TILE_FULL;
-    lstore();
-    __syncthreads();
     if (it + 1 < e1) gload(pv.col[it + 1]);
     const int k0 = kt * BK;
     const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
-    if (__any(mine)) {
+    // One tile; IS_FULL is a compile-time copy of the tile's FULL flag so the
+    // element loops carry no branch.
+    auto tile = [&](auto full_tag) {
+      constexpr bool IS_FULL = decltype(full_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         floatx16 s = floatx16{}, dp = floatx16{};
         const int roff = (32 * kb + sigma32(l32)) * KS + 8 * g;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[roff + 16 * c]), qf[c], s);
-          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[roff + 16 * c]), dof[c], dp);
+          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][roff + 16 * c]), qf[c], s);
+          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[buf][roff + 16 * c]), dof[c], dp);
         }
         // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
+        const int lo_rel = lo - k0 - 32 * kb - 8 * g, hi_rel = hi - k0 - 32 * kb - 8 * g;
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(s[r] * c2 - lse2);
-          if (!full) {
-            const int kp = k0 + 32 * kb + kappa32(r, g);
-            pr = (kp >= lo && kp <= hi) ? pr : 0.f;
+          float pr = fast_exp2(fmaf(s[r], c2, -lse2));
+          if (!IS_FULL) {
+            const int cr = 16 * (r >> 3) + (r & 7);  // key offset beyond 32*kb + 8*g
+            pr = (cr >= lo_rel && cr <= hi_rel) ? pr : 0.f;
           }
           ds[r] = pr * (dp[r] - dsum);
         }
@@ -169,13 +175,19 @@ __global__ __launch_bounds__(BQ * 2) void bwd_dq_kernel(BwdParams p) {
         for (int h8 = 0; h8 < 2; ++h8) {
           const bf16x8 db = pack_bf16x8(&ds[8 * h8]);
 #pragma unroll
-          for (int fb = 0; fb < 2; ++fb) {
-            const bf16* arow = &kts[(32 * fb + sigma32(l32)) * TS + 32 * kb + 16 * h8 + 8 * g];
-            dqa[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(arow), db, dqa[fb]);
-          }
+          for (int fb = 0; fb < 2; ++fb)
+            dqa[fb] = mfma_bf16(load_a_transposed(ks[buf], KS, 32 * kb + 16 * h8, 32 * fb, lane),
+                                db, dqa[fb]);
         }
       }
+    };
+    if (__any(mine)) {
+      if (full)
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
+    if (it + 1 < e1) lstore(buf ^ 1);
     __syncthreads();
   }
 
@@ -206,18 +218,15 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NSTEP = BQ / QS;
   constexpr int NQB = QS / 32;
   constexpr int RS = kD + 8;  // row stride of Q / dO in LDS
-  constexpr int TS = QS + 8;  // row stride of Q^T / dO^T in LDS
   constexpr int CPT = QS * 8 / NT;
   static_assert(CPT >= 1 && (QS * 8) % NT == 0, "tile/wave mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 sq[QS * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sqt[kD * TS];
-  __shared__ __attribute__((aligned(16))) bf16 sdo[QS * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sdot[kD * TS];
-  __shared__ __attribute__((aligned(16))) float slse[QS];
-  __shared__ __attribute__((aligned(16))) float sdd[QS];
-  __shared__ __attribute__((aligned(16))) int32_t slo[QS];
-  __shared__ __attribute__((aligned(16))) int32_t shi[QS];
+  __shared__ __attribute__((aligned(16))) bf16 sq[2][QS * RS];
+  __shared__ __attribute__((aligned(16))) bf16 sdo[2][QS * RS];
+  __shared__ __attribute__((aligned(16))) float slse[2][QS];
+  __shared__ __attribute__((aligned(16))) float sdd[2][QS];
+  __shared__ __attribute__((aligned(16))) int32_t slo[2][QS];
+  __shared__ __attribute__((aligned(16))) int32_t shi[2][QS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -273,40 +282,36 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     if (tid < QS) {
       const int r = r0 + tid;
       const int tk = pv.qmap[r];
-      lo_r = pv.lo[r];
-      hi_r = pv.hi[r];
+      // FULL tiles stage open bounds so that one branch-free mask serves both.
+      const bool full_tile = pv.bflag[e] == SA_TILE_FULL;
+      lo_r = full_tile ? INT_MIN : pv.lo[r];
+      hi_r = full_tile ? INT_MAX : pv.hi[r];
       lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : 0.f;
       dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      *reinterpret_cast<u32x4*>(&sq[j * RS + cc * 8]) = qreg[i];
-      *reinterpret_cast<u32x4*>(&sdo[j * RS + cc * 8]) = doreg[i];
-      const bf16x8 a = __builtin_bit_cast(bf16x8, qreg[i]);
-      const bf16x8 d = __builtin_bit_cast(bf16x8, doreg[i]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        sqt[(cc * 8 + t) * TS + j] = a[t];
-        sdot[(cc * 8 + t) * TS + j] = d[t];
-      }
+      *reinterpret_cast<u32x4*>(&sq[buf][j * RS + cc * 8]) = qreg[i];
+      *reinterpret_cast<u32x4*>(&sdo[buf][j * RS + cc * 8]) = doreg[i];
     }
     if (tid < QS) {
-      slse[tid] = lse_r;
-      sdd[tid] = dd_r;
-      slo[tid] = lo_r;
-      shi[tid] = hi_r;
+      slse[buf][tid] = lse_r;
+      sdd[buf][tid] = dd_r;
+      slo[buf][tid] = lo_r;
+      shi[buf][tid] = hi_r;
     }
   };
 
-  if (nsteps > 0) gload(0);
+  if (nsteps > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    const int e = c0 + step / NSTEP;
-    const bool full = pv.bflag[e] == SA_TILE_FULL;
-    lstore();
-    __syncthreads();
+    const int buf = step & 1;
     if (step + 1 < nsteps) gload(step + 1);
 
 #pragma unroll
@@ -315,28 +320,31 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       const int roff = (32 * qb + sigma32(l32)) * RS + 8 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[roff + 16 * c]), kq[c], s);
-        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[roff + 16 * c]), vq[c], dp);
+        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[buf][roff + 16 * c]), kq[c], s);
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[buf][roff + 16 * c]), vq[c], dp);
       }
       // Register r of half g: query 32*qb + kappa(r, g); lane = key.
       float pr[16], ds[16];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const int qloc = 32 * qb + 16 * h8 + 8 * g;
-        const floatx4 la = *reinterpret_cast<const floatx4*>(&slse[qloc]);
-        const floatx4 lb = *reinterpret_cast<const floatx4*>(&slse[qloc + 4]);
-        const floatx4 da = *reinterpret_cast<const floatx4*>(&sdd[qloc]);
-        const floatx4 db = *reinterpret_cast<const floatx4*>(&sdd[qloc + 4]);
+        const floatx4 la = *reinterpret_cast<const floatx4*>(&slse[buf][qloc]);
+        const floatx4 lb = *reinterpret_cast<const floatx4*>(&slse[buf][qloc + 4]);
+        const floatx4 da = *reinterpret_cast<const floatx4*>(&sdd[buf][qloc]);
+        const floatx4 db = *reinterpret_cast<const floatx4*>(&sdd[buf][qloc + 4]);
+        const int4 loa = *reinterpret_cast<const int4*>(&slo[buf][qloc]);
+        const int4 lob = *reinterpret_cast<const int4*>(&slo[buf][qloc + 4]);
+        const int4 hia = *reinterpret_cast<const int4*>(&shi[buf][qloc]);
+        const int4 hib = *reinterpret_cast<const int4*>(&shi[buf][qloc + 4]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * h8 + j;
           const float l2 = j < 4 ? la[j] : lb[j - 4];
           const float dd = j < 4 ? da[j] : db[j - 4];
-          float pp = fast_exp2(s[r] * c2 - l2);
-          if (!full) {
-            const int qi = qloc + j;
-            pp = (kpos >= slo[qi] && kpos <= shi[qi]) ? pp : 0.f;
-          }
+          const int qlo = j < 4 ? loa[j] : lob[j - 4];
+          const int qhi = j < 4 ? hia[j] : hib[j - 4];
+          float pp = fast_exp2(fmaf(s[r], c2, -l2));
+          pp = (kpos >= qlo && kpos <= qhi) ? pp : 0.f;
           pr[r] = pp;
           ds[r] = pp * (dp[r] - dd);
         }
@@ -347,12 +355,13 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 sb = pack_bf16x8(&ds[8 * h8]);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
-          const int trow = (32 * fb + sigma32(l32)) * TS + 32 * qb + 16 * h8 + 8 * g;
-          dva[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdot[trow]), pb, dva[fb]);
-          dka[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sqt[trow]), sb, dka[fb]);
+          const int q0 = 32 * qb + 16 * h8;
+          dva[fb] = mfma_bf16(load_a_transposed(sdo[buf], RS, q0, 32 * fb, lane), pb, dva[fb]);
+          dka[fb] = mfma_bf16(load_a_transposed(sq[buf], RS, q0, 32 * fb, lane), sb, dka[fb]);
         }
       }
     }
+    if (step + 1 < nsteps) lstore(buf ^ 1);
     __syncthreads();
   }
 

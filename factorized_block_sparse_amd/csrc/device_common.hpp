@@ -47,6 +47,41 @@ __device__ __forceinline__ floatx16 mfma_f32(float a, float b, floatx16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Transposed A operand from a row-major LDS tile (gfx950 transposing LDS read).
+//
+// ds_read_b64_tr_b16 works on groups of 16 lanes: with lane j of a group
+// addressing four consecutive 16-bit values D[j][0..3], lane i of the group
+// receives D[4*s + i/4][i%4] for s = 0..3.  If lane j addresses row
+// k0 + 8*g + j/4 of a row-major matrix M at column c0 + 16*q + 4*swap2(j%4)
+// (g = lane/32, q = (lane/16)&1, swap2 exchanges the two bits of j%4), lane i
+// receives M[k0 + 8*g + s][c0 + sigma32(16*q + i)]: one column over four
+// consecutive rows.  Two such reads (rows +0..3 and +4..7) give the A operand
+// of a 32x32x16 MFMA for A[row][k] = M[k0 + k][c0 + sigma32(row)], i.e. the
+// transposed tile, with the same sigma row order as the row-major loads.
+// stride is the row stride of M in elements (a multiple of 4).
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ v4i16 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) bf16*)(p)));
+}
+
+__device__ __forceinline__ bf16x8 load_a_transposed(const bf16* m, int stride, int k0, int c0,
+                                                    int lane) {
+  const int g = lane >> 5, q = (lane >> 4) & 1, j = lane & 15;
+  const int t = j & 3;
+  const int tsw = ((t & 1) << 1) | (t >> 1);
+  const bf16* p0 = m + (k0 + 8 * g + (j >> 2)) * stride + c0 + 16 * q + 4 * tsw;
+  const v4i16 a = lds_read_tr16(p0);
+  const v4i16 b = lds_read_tr16(p0 + 4 * stride);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
 // Value of lane L ^ 32 (the other half of the wave).
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -5,14 +5,17 @@
 // ("Sparse Transformers 深度解读报告", section 3.5: blocked sub-blocks of
 // Q/K/V, the softmax fused into a single kernel with its intermediates in
 // registers, masked-out tiles never computed).  Per key tile:
-//   1. K rows (through the pattern's key map) are staged into LDS row-major
-//      and V rows transposed (V^T), double-buffered, one barrier per tile;
+//   1. K and V rows (through the pattern's key map) are staged into LDS
+//      row-major, double-buffered, one barrier per tile; V^T reaches the MFMA
+//      through transposing LDS reads;
 //   2. each wave owns 32 query rows and computes S^T = K Q^T on the MFMA
 //      units (fp32 accumulation; Q stays in registers for the whole walk);
 //   3. on PARTIAL tiles the fine mask is two integer compares against the
 //      row's key interval; FULL tiles apply no mask;
-//   4. running max / sum update (base-2 exponentials with the softmax scale
-//      folded in), rescale of the output accumulator;
+//   4. running max / sum update in base 2 with the softmax scale folded into
+//      one FMA per score; the running max (and the rescale of the output
+//      accumulator) only moves when a tile's max exceeds it by more than
+//      2^kRescaleLog2, so P <= 2^kRescaleLog2 and most tiles skip the rescale;
 //   5. O^T += V^T P^T on the MFMA units, P rounded to the input type.
 // The epilogue writes O rows (through the query map) and the per-row
 // log-sum-exp that the backward pass rebuilds probabilities from (report
@@ -38,8 +41,9 @@ struct FwdParams {
 };
 
 constexpr float kNegInit = -3.0e38f;  // running-max start: exp2(kNegInit - x) == 0
-constexpr float kMasked = -1.0e30f;   // masked logit in the base-2 domain
+constexpr float kMasked = -1.0e30f;   // masked logit in the base-2 domain (float32 path)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
 
 // --------------------------------------------------------------------------
 // bfloat16 inputs, 32x32x16 bf16 MFMA
@@ -49,12 +53,11 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
-  constexpr int KS = kD + 8;  // LDS row stride of K (elements)
-  constexpr int VS = BK + 8;  // LDS row stride of V^T (elements)
+  constexpr int KS = kD + 8;  // LDS row stride of K and V (elements)
   constexpr int CPT = BK * 8 / NT;  // 16-byte chunks per thread and tensor
   static_assert(CPT >= 1 && (BK * 8) % NT == 0, "tile/wave mismatch");
   __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) bf16 vt[2][kD * VS];
+  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * KS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -102,9 +105,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT, j = c >> 3, cc = c & 7;
       *reinterpret_cast<u32x4*>(&ks[buf][j * KS + cc * 8]) = kreg[i];
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vreg[i]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) vt[buf][(cc * 8 + t) * VS + j] = vv[t];
+      *reinterpret_cast<u32x4*>(&vs[buf][j * KS + cc * 8]) = vreg[i];
     }
   };
 
@@ -136,45 +137,45 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
         for (int c = 0; c < 4; ++c)
           s[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(krow + 16 * c), qf[c], s[kb]);
       }
-      float mx = kNegInit;
-      if (full) {
+      if (!full) {
+        // Key k0 + c is visible iff lo <= k0 + c <= hi; c = 32*kb + kappa(r, g)
+        // = 8*g + (a constant per register).
+        const int lo_rel = lo - k0 - 8 * g, hi_rel = hi - k0 - 8 * g;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            s[kb][r] *= c2;
-            mx = fmaxf(mx, s[kb][r]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kp = k0 + 32 * kb + kappa32(r, g);
-            const float x = (kp >= lo && kp <= hi) ? s[kb][r] * c2 : kMasked;
-            s[kb][r] = x;
-            mx = fmaxf(mx, x);
+            const int cr = 32 * kb + 16 * (r >> 3) + (r & 7);
+            s[kb][r] = (cr >= lo_rel && cr <= hi_rel) ? s[kb][r] : -INFINITY;
           }
       }
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
+      float mx = -INFINITY;  // max of the raw scores (scale > 0)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, other_half(mx)) * c2;
+      if (__any(mx > m_run + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          oacc[0][r] *= alpha;
+          oacc[1][r] *= alpha;
+        }
+        m_run = m_new;
+      }
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(s[kb][r] - m_new);
+          const float pr = fast_exp2(fmaf(s[kb][r], c2, -m_run));
           s[kb][r] = pr;
           lsum += pr;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        oacc[0][r] *= alpha;
-        oacc[1][r] *= alpha;
-      }
+      l_run += lsum;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -184,10 +185,9 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
           for (int j = 0; j < 8; ++j) tmp[j] = s[kb][8 * h8 + j];
           const bf16x8 pb = pack_bf16x8(tmp);
 #pragma unroll
-          for (int fb = 0; fb < 2; ++fb) {
-            const bf16* vrow = &vt[buf][(32 * fb + sigma32(l32)) * VS + 32 * kb + 16 * h8 + 8 * g];
-            oacc[fb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(vrow), pb, oacc[fb]);
-          }
+          for (int fb = 0; fb < 2; ++fb)
+            oacc[fb] = mfma_bf16(load_a_transposed(vs[buf], KS, 32 * kb + 16 * h8, 32 * fb, lane),
+                                 pb, oacc[fb]);
         }
       }
     }
