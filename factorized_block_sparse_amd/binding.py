@@ -25,6 +25,7 @@ SA_BF16, SA_FP32 = 0, 1
 SA_SELF_IF_EMPTY = 1
 SA_BLOB_MAGIC = 0x31415053
 SA_TILE_PARTIAL, SA_TILE_FULL = 0, 1
+SA_XCDS = 8
 
 EXPORTED = (
     "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd",
@@ -65,6 +66,8 @@ class CBlobHeader(ctypes.Structure):
                 ("fwd_sched_len", ctypes.c_int32), ("bwd_sched_len", ctypes.c_int32),
                 ("red_sched_off", ctypes.c_int64), ("red_sched_len", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32),
+                ("fwd_xl_off", ctypes.c_int64), ("bwd_xl_off", ctypes.c_int64),
+                ("fwd_xl_len", ctypes.c_int32), ("bwd_xl_len", ctypes.c_int32),
                 ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64)]
 
 
@@ -205,6 +208,12 @@ class Layout:
     def bwd_schedule(self) -> np.ndarray:
         """Rows (head, k-tile, first CSC entry, end CSC entry, partial slot or -1)."""
         return self._arr(self.header.bwd_sched_off, 5 * self.header.bwd_sched_len, np.int32).reshape(-1, 5)
+
+    def xcd_lists(self, which: str) -> np.ndarray:
+        """[SA_XCDS, len] schedule indices per XCD ("fwd" or "bwd"), -1 = padding."""
+        h = self.header
+        off, ln = (h.fwd_xl_off, h.fwd_xl_len) if which == "fwd" else (h.bwd_xl_off, h.bwd_xl_len)
+        return self._arr(off, SA_XCDS * ln, np.int32).reshape(SA_XCDS, ln)
 
     def reduce_schedule(self) -> np.ndarray:
         """Rows (head, k-tile, first partial slot, chunks) of the split key tiles."""

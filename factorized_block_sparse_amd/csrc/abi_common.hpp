@@ -14,6 +14,8 @@ struct LaunchInfo {
   int32_t block_q, block_k, num_heads, n_pad, nqt, nkt;
   int32_t fwd_sched_len, bwd_sched_len;
   int64_t fwd_sched_off, bwd_sched_off, total_bytes;
+  int64_t fwd_xl_off, bwd_xl_off;
+  int32_t fwd_xl_len, bwd_xl_len;
 };
 
 inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -46,6 +48,10 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   li->fwd_sched_off = h.fwd_sched_off;
   li->bwd_sched_off = h.bwd_sched_off;
   li->total_bytes = h.total_bytes;
+  li->fwd_xl_off = h.fwd_xl_off;
+  li->bwd_xl_off = h.bwd_xl_off;
+  li->fwd_xl_len = h.fwd_xl_len;
+  li->bwd_xl_len = h.bwd_xl_len;
   return SA_OK;
 }
 

@@ -39,6 +39,9 @@ struct BwdParams {
   const int32_t* qsched;    // (head, q-tile) pairs: the forward schedule
   const int32_t* ksched;    // (head, k-tile, e0, e1, slot)
   const int32_t* rsched;    // (head, k-tile, slot0, chunks)
+  const int32_t* qxl;       // per-XCD lists over qsched
+  const int32_t* kxl;       // per-XCD lists over ksched
+  int32_t qxl_len, kxl_len;
   int32_t B, H, n, num_slots;
   const bf16* q;
   const bf16* k;
@@ -59,7 +62,7 @@ struct BwdParams {
 // dQ pass: one workgroup per query tile, BQ = 32 * NW rows, key tiles of BK.
 // --------------------------------------------------------------------------
 template <int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
@@ -71,8 +74,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
+  int b, item;
+  if (!xcd_work_item(p.qxl, p.qxl_len, p.B, &b, &item)) return;
   const int head = p.qsched[2 * item], qt = p.qsched[2 * item + 1];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
@@ -230,8 +233,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
+  int b, item;
+  if (!xcd_work_item(p.kxl, p.kxl_len, p.B, &b, &item)) return;
   const int32_t* it5 = p.ksched + 5 * item;
   const int head = it5[0], kt = it5[1], c0 = it5[2], c1 = it5[3], slot = it5[4];
   const PatView pv = pattern_of_head(p.blob, head);
@@ -499,8 +502,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return SA_EINVAL;
-  const int64_t gq = int64_t(li.fwd_sched_len) * B;
-  const int64_t gk = int64_t(li.bwd_sched_len) * B;
+  const int64_t gq = int64_t(SA_XCDS) * li.fwd_xl_len * B;
+  const int64_t gk = int64_t(SA_XCDS) * li.bwd_xl_len * B;
   const int64_t gr = int64_t(h.red_sched_len) * B;
   if (gq > INT32_MAX || gk > INT32_MAX || gr > INT32_MAX) return SA_EUNSUPPORTED;
 
@@ -509,6 +512,10 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.qsched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
   prm.ksched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
   prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
+  prm.qxl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
+  prm.kxl = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xl_off);
+  prm.qxl_len = li.fwd_xl_len;
+  prm.kxl_len = li.bwd_xl_len;
   prm.B = B;
   prm.H = H;
   prm.n = int32_t(li.n);

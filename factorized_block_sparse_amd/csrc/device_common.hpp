@@ -136,12 +136,16 @@ __device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head
   return v;
 }
 
-// Host-side copy of the few header fields the launchers need.
-struct HostLayoutInfo {
-  int64_t n;
-  int32_t block_q, block_k, num_heads, n_pad, nqt, nkt;
-  int32_t fwd_sched_len, bwd_sched_len;
-  int64_t fwd_sched_off, bwd_sched_off;
-};
+// Workgroup -> (batch element, schedule entry) through the per-XCD lists of
+// the layout (workgroup w runs on XCD w % SA_XCDS).  Launch grids are
+// SA_XCDS * len * B workgroups; false = padding, nothing to do.
+__device__ __forceinline__ bool xcd_work_item(const int32_t* xl, int len, int B, int* b,
+                                              int* item) {
+  const int w = int(blockIdx.x);
+  const int x = w % SA_XCDS, j = w / SA_XCDS;
+  *b = j / len;
+  *item = xl[x * len + j % len];
+  return *item >= 0 && *b < B;
+}
 
 }  // namespace sa

@@ -31,6 +31,8 @@ namespace sa {
 struct FwdParams {
   const uint8_t* blob;
   const int32_t* sched;  // (head, q-tile) pairs
+  const int32_t* xl;     // per-XCD lists of schedule entries
+  int32_t xl_len;
   int32_t B, H, n;
   const void* q;
   const void* k;
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
+  int b, item;
+  if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
   const int head = p.sched[2 * item], qt = p.sched[2 * item + 1];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
@@ -229,8 +231,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
+  int b, item;
+  if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
   const int head = p.sched[2 * item], qt = p.sched[2 * item + 1];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
@@ -381,15 +383,17 @@ extern "C" int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int 
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
-  if (B == 0 || li.fwd_sched_len == 0) return SA_OK;  // empty batch: pointers may be NULL
+  if (B == 0 || li.fwd_xl_len == 0) return SA_OK;  // empty batch: pointers may be NULL
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return SA_EINVAL;
-  const int64_t grid = int64_t(li.fwd_sched_len) * B;
+  const int64_t grid = int64_t(SA_XCDS) * li.fwd_xl_len * B;
   if (grid > INT32_MAX) return SA_EUNSUPPORTED;
 
   FwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
   prm.sched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
+  prm.xl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
+  prm.xl_len = li.fwd_xl_len;
   prm.B = B;
   prm.H = H;
   prm.n = int32_t(li.n);

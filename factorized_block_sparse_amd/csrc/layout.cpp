@@ -225,9 +225,48 @@ struct SchedItem {
   int32_t e0 = 0, e1 = 0, slot = -1;
 };
 
+// Per-XCD lists over the sorted schedule `sorted` (work in sorted order):
+// the items are taken in natural order (head, tile, e0), cut into SA_XCDS
+// contiguous runs of about equal work, each run sorted heaviest first, and
+// every list padded with -1 to the longest.  Returns the list length.
+int32_t xcd_lists(const std::vector<SchedItem>& sorted, std::vector<int32_t>& out) {
+  const int32_t n = int32_t(sorted.size());
+  std::vector<int32_t> order(n);
+  for (int32_t i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    const SchedItem &x = sorted[a], &y = sorted[b];
+    if (x.head != y.head) return x.head < y.head;
+    if (x.tile != y.tile) return x.tile < y.tile;
+    return x.e0 < y.e0;
+  });
+  int64_t total = 0;
+  for (const auto& it : sorted) total += it.work;
+  std::vector<std::vector<int32_t>> lists(SA_XCDS);
+  int64_t run = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t idx = order[i];
+    // XCD of the item's work midpoint
+    const int64_t mid2 = 2 * run + sorted[idx].work;
+    int32_t x = total > 0 ? int32_t(mid2 * SA_XCDS / (2 * total)) : 0;
+    x = std::min<int32_t>(std::max<int32_t>(x, 0), SA_XCDS - 1);
+    lists[x].push_back(idx);
+    run += sorted[idx].work;
+  }
+  int32_t len = 0;
+  for (auto& l : lists) {
+    // indices into `sorted` ascend with decreasing work: sorting them keeps heaviest first
+    std::sort(l.begin(), l.end());
+    len = std::max<int32_t>(len, int32_t(l.size()));
+  }
+  out.assign(size_t(SA_XCDS) * len, -1);
+  for (int32_t x = 0; x < SA_XCDS; ++x)
+    for (size_t j = 0; j < lists[x].size(); ++j) out[size_t(x) * len + j] = lists[x][j];
+  return len;
+}
+
 // Heaviest first; ties keep (head, tile) order.  `fields` = 2 (head, tile) or
 // 5 (head, tile, e0, e1, slot).
-std::vector<int32_t> sorted_schedule(std::vector<SchedItem> items, int fields) {
+std::vector<int32_t> sorted_schedule(std::vector<SchedItem>& items, int fields) {
   std::stable_sort(items.begin(), items.end(),
                    [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
   std::vector<int32_t> out;
@@ -317,6 +356,9 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   }
   const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items, 2);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items, 5);
+  std::vector<int32_t> fwd_xl, bwd_xl;
+  const int32_t fwd_xl_len = xcd_lists(fwd_items, fwd_xl);
+  const int32_t bwd_xl_len = xcd_lists(bwd_items, bwd_xl);
 
   // Two passes: size, then write.
   for (int pass = 0; pass < 2; ++pass) {
@@ -330,6 +372,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.fwd_sched_off = w.put(fwd_sched);
     hdr.bwd_sched_off = w.put(bwd_sched);
     hdr.red_sched_off = w.put(red_sched);
+    hdr.fwd_xl_off = w.put(fwd_xl);
+    hdr.bwd_xl_off = w.put(bwd_xl);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
       sa_pattern_rec& r = recs[i];
@@ -382,6 +426,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwd_sched_len = int32_t(bwd_items.size());
     hdr.red_sched_len = int32_t(red_sched.size() / 4);
     hdr.num_slots = num_slots;
+    hdr.fwd_xl_len = fwd_xl_len;
+    hdr.bwd_xl_len = bwd_xl_len;
     hdr.pairs_all_heads = pairs_all;
     hdr.tiles_all_heads = tiles_all;
     std::memcpy(blob + hdr_at, &hdr, sizeof(hdr));
@@ -425,7 +471,9 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
       !in_blob(h.pattern_off, int64_t(sizeof(sa_pattern_rec)) * h.num_patterns, total) ||
       !in_blob(h.fwd_sched_off, 8 * int64_t(h.fwd_sched_len), total) ||
       !in_blob(h.bwd_sched_off, 20 * int64_t(h.bwd_sched_len), total) ||
-      !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0)
+      !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0 ||
+      !in_blob(h.fwd_xl_off, 4 * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
+      !in_blob(h.bwd_xl_off, 4 * int64_t(SA_XCDS) * h.bwd_xl_len, total))
     return SA_EINVAL;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

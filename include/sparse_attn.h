@@ -110,11 +110,14 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 2u
+#define SA_BLOB_VERSION 3u
 /* Key tiles read by more than this many query rows are split into chunks for
  * the dK/dV pass (each chunk a workgroup); their partial sums are reduced in a
  * fixed order. */
 #define SA_SPLIT_ROWS 1536
+/* Number of accelerator complex dies (XCDs, each with its own L2) that
+ * workgroups are dealt to round-robin on MI355X. */
+#define SA_XCDS 8
 #define SA_TILE_PARTIAL 0u
 #define SA_TILE_FULL 1u
 
@@ -154,6 +157,15 @@ typedef struct {
   int64_t red_sched_off;    /* int32[4 * red_sched_len]: (head, k-tile, first slot, chunks) */
   int32_t red_sched_len;
   int32_t num_slots;        /* partial slots per batch element */
+  /* Per-XCD launch order.  Workgroup w of a launch runs on XCD w % SA_XCDS
+   * (round-robin dispatch); its batch element and schedule entry are
+   * b = (w / SA_XCDS) / len and xl[(w % SA_XCDS) * len + (w / SA_XCDS) % len]
+   * (-1 = nothing to do).  Each XCD's list is a contiguous run of the
+   * (head, tile) work in natural order -- so an XCD's L2 holds few heads --
+   * sorted heaviest first and padded to the common length. */
+  int64_t fwd_xl_off;       /* int32[SA_XCDS * fwd_xl_len], indices into fwd_sched */
+  int64_t bwd_xl_off;       /* int32[SA_XCDS * bwd_xl_len], indices into bwd_sched */
+  int32_t fwd_xl_len, bwd_xl_len;
   int64_t pairs_all_heads;  /* sum of pairs over the heads (one batch element) */
   int64_t tiles_all_heads;  /* sum of active tiles over the heads */
 } sa_blob_header;

@@ -137,6 +137,34 @@ def test_schedules_cover_every_tile_heaviest_first():
 
 
 @pytest.mark.parametrize("n,bq,bk,heads", [
+    (12288, 128, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0)] * 4),
+    (3072, 64, 64, [HeadPattern("local", 64), HeadPattern("stride", 64)] * 4),
+    (100, 32, 32, [HeadPattern("local", 5)]),
+])
+def test_xcd_lists_cover_every_schedule_entry_once(n, bq, bk, heads):
+    """Per-XCD lists: a permutation of the schedule (plus -1 padding), heaviest first per list,
+    each list a contiguous run of the (head, tile) natural order."""
+    lay = Layout(n, heads, bq, bk)
+    for which, sched in (("fwd", lay.fwd_schedule()), ("bwd", lay.bwd_schedule())):
+        xl = lay.xcd_lists(which)
+        assert xl.shape[0] == bd.SA_XCDS
+        flat = xl[xl >= 0]
+        assert sorted(flat.tolist()) == list(range(len(sched)))
+        keys = [tuple(sched[i][:2]) + ((int(sched[i][2]),) if which == "bwd" else ()) for i in range(len(sched))]
+        natural = sorted(range(len(sched)), key=lambda i: keys[i])
+        rank = {i: r for r, i in enumerate(natural)}
+        prev_max = -1
+        for row in xl:
+            ids = [int(i) for i in row if i >= 0]
+            assert ids == sorted(ids)  # heaviest first = ascending schedule index
+            if ids:
+                rs = sorted(rank[i] for i in ids)
+                assert rs == list(range(rs[0], rs[0] + len(rs)))  # contiguous run
+                assert rs[0] > prev_max
+                prev_max = rs[-1]
+
+
+@pytest.mark.parametrize("n,bq,bk,heads", [
     (12288, 64, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
                      HeadPattern("summary", 128, 32, 3)]),
     (5000, 32, 32, [HeadPattern("summary", 64, 4, 1), HeadPattern("local", 3000)]),
