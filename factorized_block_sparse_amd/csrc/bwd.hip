@@ -111,11 +111,16 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 
   const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
   u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int kt) {
+  int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
+  auto iload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) kidx[i] = pv.kmap[kt * BK + ((tid + i * NT) >> 3)];
+  };
+  auto gload = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      const int tk = pv.kmap[kt * BK + j];
+      const int cc = (tid + i * NT) & 7;
+      const int tk = kidx[i];
       if (tk >= 0) {
         kreg[i] = reinterpret_cast<const u32x4*>(p.k + (base + tk) * kD)[cc];
         vreg[i] = reinterpret_cast<const u32x4*>(p.v + (base + tk) * kD)[cc];
@@ -138,15 +143,20 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   dqa[0] = dqa[1] = floatx16{};
   const float c2 = p.scale_log2;
   if (e0 < e1) {
-    gload(pv.col[e0]);
+    iload(pv.col[e0]);
+    gload();
     lstore(0);
+    if (e0 + 1 < e1) iload(pv.col[e0 + 1]);
   }
   __syncthreads();
   for (int it = e0; it < e1; ++it) {
     const int buf = (it - e0) & 1;
     const int kt = pv.col[it];
     const bool full = pv.fflag[it] == SA_TILE_FULL;
-    if (it + 1 < e1) gload(pv.col[it + 1]);
+    if (it + 1 < e1) {
+      gload();                                   // tile it+1, indices already here
+      if (it + 2 < e1) iload(pv.col[it + 2]);    // indices of tile it+2
+    }
     const int k0 = kt * BK;
     const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
     // One tile; IS_FULL is a compile-time copy of the tile's FULL flag so the
@@ -267,13 +277,21 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   u32x4 qreg[CPT], doreg[CPT];
   float lse_r = 0.f, dd_r = 0.f;
   int lo_r = 1, hi_r = 0;
+  int qidx[CPT], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
+  auto iload = [&](int step) {
+    const int e = c0 + step / NSTEP;
+    const int r0 = pv.row[e] * BQ + (step % NSTEP) * QS;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) qidx[i] = pv.qmap[r0 + ((tid + i * NT) >> 3)];
+    if (tid < QS) rtok = pv.qmap[r0 + tid];
+  };
   auto gload = [&](int step) {
     const int e = c0 + step / NSTEP;
     const int r0 = pv.row[e] * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      const int tk = pv.qmap[r0 + j];
+      const int cc = (tid + i * NT) & 7;
+      const int tk = qidx[i];
       if (tk >= 0) {
         qreg[i] = reinterpret_cast<const u32x4*>(p.q + (base + tk) * kD)[cc];
         doreg[i] = reinterpret_cast<const u32x4*>(p.dout + (base + tk) * kD)[cc];
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     }
     if (tid < QS) {
       const int r = r0 + tid;
-      const int tk = pv.qmap[r];
+      const int tk = rtok;
       // FULL tiles stage open bounds so that one branch-free mask serves both.
       const bool full_tile = pv.bflag[e] == SA_TILE_FULL;
       lo_r = full_tile ? INT_MIN : pv.lo[r];
@@ -309,13 +327,18 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   };
 
   if (nsteps > 0) {
+    iload(0);
     gload(0);
     lstore(0);
+    if (nsteps > 1) iload(1);
   }
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
+    if (step + 1 < nsteps) {
+      gload(step + 1);                       // indices already here
+      if (step + 2 < nsteps) iload(step + 2);
+    }
 
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {

@@ -88,11 +88,16 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
   u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int kt) {
+  int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
+  auto iload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) kidx[i] = pv.kmap[kt * BK + ((tid + i * NT) >> 3)];
+  };
+  auto gload = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      const int tk = pv.kmap[kt * BK + j];
+      const int cc = (tid + i * NT) & 7;
+      const int tk = kidx[i];
       if (tk >= 0) {
         kreg[i] = reinterpret_cast<const u32x4*>(kg + size_t(tk) * kD)[cc];
         vreg[i] = reinterpret_cast<const u32x4*>(vg + size_t(tk) * kD)[cc];
@@ -118,15 +123,20 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
   const float c2 = p.scale_log2;
 
   if (e0 < e1) {
-    gload(pv.col[e0]);
+    iload(pv.col[e0]);
+    gload();
     lstore(0);
+    if (e0 + 1 < e1) iload(pv.col[e0 + 1]);
   }
   __syncthreads();
   for (int it = e0; it < e1; ++it) {
     const int buf = (it - e0) & 1;
     const int kt = pv.col[it];
     const bool full = pv.fflag[it] == SA_TILE_FULL;
-    if (it + 1 < e1) gload(pv.col[it + 1]);
+    if (it + 1 < e1) {
+      gload();                                   // tile it+1, indices already here
+      if (it + 2 < e1) iload(pv.col[it + 2]);    // indices of tile it+2
+    }
     const int k0 = kt * BK;
     const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
     if (__any(mine)) {
