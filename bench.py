@@ -51,7 +51,7 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
         return 2 * D * pairs, rows * (5 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
     if label == "bwd_dkdv":
         return 6 * D * pairs, rows * (6 * D * 2 + 8)             # Q,K,V,dO read, dK,dV write; LSE, D
-    if label == "bwd_reduce":
+    if label in ("fwd_combine", "bwd_reduce"):
         return 0, 0
     raise ValueError(label)
 
@@ -158,12 +158,20 @@ def main():
         inp = W.workload_inputs(w)
         inputs[w.name] = inp
         q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+        dt = bd.SA_BF16 if w.dtype == "bf16" else bd.SA_FP32
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev)
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         ws = torch.empty(bd.bwd_workspace_bytes(lay, w.B, w.H), dtype=torch.uint8, device=dev)
+        fws = torch.empty(max(1, bd.fwd_workspace_bytes(lay, w.B, w.H, dtype=dt)), dtype=torch.uint8,
+                          device=dev)
         pairs = lay.pairs_per_batch() * w.B
-        calls = [("fwd", lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse: bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse))]
+        calls = []
+        for label, ph in (("fwd", bd.SA_FWD_MAIN), ("fwd_combine", bd.SA_FWD_COMBINE)):
+            if label == "fwd_combine" and lay.header.comb_sched_len == 0:
+                continue
+            calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, fws=fws, ph=ph:
+                          bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws, phases=ph)))
         if w.backward:
             for label, ph in (("bwd_dq", bd.SA_BWD_DQ), ("bwd_dkdv", bd.SA_BWD_DKDV),
                               ("bwd_reduce", bd.SA_BWD_REDUCE)):

@@ -28,10 +28,11 @@ SA_TILE_PARTIAL, SA_TILE_FULL = 0, 1
 SA_XCDS = 8
 
 EXPORTED = (
-    "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd",
-    "sparse_attn_bwd_workspace", "sparse_attn_bwd", "sparse_attn_bwd_phases",
-    "sparse_attn_strerror",
+    "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd_workspace",
+    "sparse_attn_fwd", "sparse_attn_fwd_phases", "sparse_attn_bwd_workspace",
+    "sparse_attn_bwd", "sparse_attn_bwd_phases", "sparse_attn_strerror",
 )
+SA_FWD_MAIN, SA_FWD_COMBINE, SA_FWD_ALL = 1, 2, 3
 SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_REDUCE, SA_BWD_ALL = 1, 2, 4, 7
 
 
@@ -43,7 +44,8 @@ class CHeadPattern(ctypes.Structure):
 class CLayoutDesc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("heads", ctypes.POINTER(CHeadPattern)),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("split_keys", ctypes.c_int32),
+                ("split_rows", ctypes.c_int32)]
 
 
 class CPatternRec(ctypes.Structure):
@@ -68,6 +70,9 @@ class CBlobHeader(ctypes.Structure):
                 ("num_slots", ctypes.c_int32),
                 ("fwd_xl_off", ctypes.c_int64), ("bwd_xl_off", ctypes.c_int64),
                 ("fwd_xl_len", ctypes.c_int32), ("bwd_xl_len", ctypes.c_int32),
+                ("comb_sched_off", ctypes.c_int64), ("comb_sched_len", ctypes.c_int32),
+                ("num_qslots", ctypes.c_int32),
+                ("split_keys", ctypes.c_int32), ("split_rows", ctypes.c_int32),
                 ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64)]
 
 
@@ -101,8 +106,13 @@ def load_library():
         lib.sparse_attn_layout.restype = i32
         lib.sparse_attn_layout_check.argtypes = [vp, sz]
         lib.sparse_attn_layout_check.restype = i32
-        lib.sparse_attn_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, f32, vp]
+        lib.sparse_attn_fwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.sparse_attn_fwd_workspace.restype = i32
+        lib.sparse_attn_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, f32, vp]
         lib.sparse_attn_fwd.restype = i32
+        lib.sparse_attn_fwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
+                                               f32, ctypes.c_uint, vp]
+        lib.sparse_attn_fwd_phases.restype = i32
         lib.sparse_attn_bwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
         lib.sparse_attn_bwd_workspace.restype = i32
         lib.sparse_attn_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -144,13 +154,17 @@ class HeadPattern:
 
 
 def sparse_attn_layout(n: int, heads, block_q: int = 64, block_k: int = 64,
-                       self_if_empty: bool = True) -> np.ndarray:
-    """Build the layout blob (host bytes) for ``heads`` at sequence length ``n``."""
+                       self_if_empty: bool = True, split_keys: int = 0,
+                       split_rows: int = 0) -> np.ndarray:
+    """Build the layout blob (host bytes) for ``heads`` at sequence length ``n``.
+
+    ``split_keys`` / ``split_rows`` are the chunk caps of the forward / dQ and
+    dK/dV schedules (0 = the library defaults)."""
     lib = load_library()
     heads = [h if isinstance(h, HeadPattern) else HeadPattern(h.kind, h.l, h.c, h.sub) for h in heads]
     arr = (CHeadPattern * max(1, len(heads)))(*[h.to_c() for h in heads])
     desc = CLayoutDesc(n, block_q, block_k, len(heads), arr,
-                       SA_SELF_IF_EMPTY if self_if_empty else 0)
+                       SA_SELF_IF_EMPTY if self_if_empty else 0, split_keys, split_rows)
     size = ctypes.c_size_t(0)
     _check(lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)), "layout size")
     blob = np.zeros(size.value, dtype=np.uint8)
@@ -163,10 +177,11 @@ class Layout:
     """A built layout: the host blob plus lazily made device copies (one per device)."""
 
     def __init__(self, n: int, heads, block_q: int = 64, block_k: int = 64,
-                 self_if_empty: bool = True):
+                 self_if_empty: bool = True, split_keys: int = 0, split_rows: int = 0):
         self.n = int(n)
         self.heads = tuple(heads)
-        self.blob = sparse_attn_layout(n, heads, block_q, block_k, self_if_empty)
+        self.blob = sparse_attn_layout(n, heads, block_q, block_k, self_if_empty, split_keys,
+                                       split_rows)
         self.header = CBlobHeader.from_buffer_copy(self.blob[: ctypes.sizeof(CBlobHeader)].tobytes())
         self._dev = {}
 
@@ -203,7 +218,12 @@ class Layout:
         }
 
     def fwd_schedule(self) -> np.ndarray:
-        return self._arr(self.header.fwd_sched_off, 2 * self.header.fwd_sched_len, np.int32).reshape(-1, 2)
+        """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot or -1)."""
+        return self._arr(self.header.fwd_sched_off, 5 * self.header.fwd_sched_len, np.int32).reshape(-1, 5)
+
+    def combine_schedule(self) -> np.ndarray:
+        """Rows (head, q-tile, first partial slot, chunks) of the split query tiles."""
+        return self._arr(self.header.comb_sched_off, 4 * self.header.comb_sched_len, np.int32).reshape(-1, 4)
 
     def bwd_schedule(self) -> np.ndarray:
         """Rows (head, k-tile, first CSC entry, end CSC entry, partial slot or -1)."""
@@ -266,18 +286,39 @@ def _check_qkv(layout: Layout, tensors, names):
     return B, H, n, d, dt
 
 
-def sparse_attn_fwd(layout: Layout, q, k, v, scale: float | None = None, out=None, lse=None):
-    """Forward on the current torch stream: returns (o, lse)."""
+def fwd_workspace_bytes(layout: Layout, B: int, H: int, d: int = 64, dtype: int = SA_BF16) -> int:
+    lib = load_library()
+    size = ctypes.c_size_t(0)
+    _check(lib.sparse_attn_fwd_workspace(layout.blob.ctypes.data, B, H, d, dtype,
+                                         ctypes.byref(size)), "sparse_attn_fwd_workspace")
+    return size.value
+
+
+def sparse_attn_fwd(layout: Layout, q, k, v, scale: float | None = None, out=None, lse=None,
+                    workspace=None, phases: int = SA_FWD_ALL):
+    """Forward on the current torch stream: returns (o, lse).
+
+    ``phases`` selects which of the two launches run (``sparse_attn_fwd_phases``
+    in the C header); the default runs both.
+    """
     import torch
     lib = load_library()
     B, H, n, d, dt = _check_qkv(layout, (q, k, v), ("q", "k", "v"))
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        need = fwd_workspace_bytes(layout, B, H, d, dt)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    ws_ptr = 0 if workspace is None else _ptr(workspace)
+    ws_len = 0 if workspace is None else workspace.numel()
     blob_dev = layout.device_blob(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.sparse_attn_fwd(layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
-                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
-                             0.0 if scale is None else float(scale), stream)
+    args = (layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt, _ptr(q), _ptr(k), _ptr(v),
+            _ptr(o), _ptr(lse_t), ws_ptr, ws_len, 0.0 if scale is None else float(scale))
+    if phases == SA_FWD_ALL:
+        rc = lib.sparse_attn_fwd(*args, stream)
+    else:
+        rc = lib.sparse_attn_fwd_phases(*args, phases, stream)
     _check(rc, "sparse_attn_fwd")
     return o, lse_t
 

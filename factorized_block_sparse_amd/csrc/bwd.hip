@@ -21,7 +21,10 @@
 //             through transposing LDS reads).  Unsplit
 //             tiles write dK, dV (exact zeros for keys no query reads); chunks
 //             of split tiles write float32 partial sums to the workspace;
-//   bwd_reduce sums the chunks of each split key tile in chunk order.
+//   bwd_reduce sums the chunks of each split key tile (dK, dV) and of each
+//             split query tile (dQ) in chunk order.
+// Long query tiles are split into chunks for the dQ pass exactly as for the
+// forward (float32 partial dQ per chunk).
 
 #include <limits.h>
 #include <math.h>
@@ -36,13 +39,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
   const uint8_t* blob;
-  const int32_t* qsched;    // (head, q-tile) pairs: the forward schedule
+  const int32_t* qsched;    // (head, q-tile, e0, e1, slot): the forward schedule
   const int32_t* ksched;    // (head, k-tile, e0, e1, slot)
   const int32_t* rsched;    // (head, k-tile, slot0, chunks)
+  const int32_t* csched;    // (head, q-tile, slot0, chunks)
   const int32_t* qxl;       // per-XCD lists over qsched
   const int32_t* kxl;       // per-XCD lists over ksched
   int32_t qxl_len, kxl_len;
-  int32_t B, H, n, num_slots;
+  int32_t B, H, n, num_slots, num_qslots, red_len;
   const bf16* q;
   const bf16* k;
   const bf16* v;
@@ -53,7 +57,8 @@ struct BwdParams {
   bf16* dk;
   bf16* dv;
   float* dsum;     // D, [B, H, n]
-  float* partial;  // [B, num_slots, 2, BK, 64]
+  float* partial;  // [B, num_slots, 2, BK, 64]: dK, dV chunks of split key tiles
+  float* part_dq;  // [B, num_qslots, BQ, 64]: dQ chunks of split query tiles
   float scale;
   float scale_log2;
 };
@@ -76,7 +81,8 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.qxl, p.qxl_len, p.B, &b, &item)) return;
-  const int head = p.qsched[2 * item], qt = p.qsched[2 * item + 1];
+  const int32_t* it5 = p.qsched + 5 * item;
+  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
@@ -109,7 +115,6 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   dsum += other_half(dsum);
   if (tok >= 0 && g == 0) p.dsum[base + tok] = dsum;
 
-  const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
   u32x4 kreg[CPT], vreg[CPT];
   int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
@@ -204,16 +209,35 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     __syncthreads();
   }
 
-  if (tok >= 0) {
-    bf16* row = p.dq + (base + tok) * kD;
+  // Register r of half g: feature 32*fb + kappa(r, g); lane = query row.
+  if (slot < 0) {
+    if (tok >= 0) {
+      bf16* row = p.dq + (base + tok) * kD;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          float tmp[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) tmp[j] = dqa[fb][8 * h8 + j] * p.scale;
+          *reinterpret_cast<bf16x8*>(row + 32 * fb + 16 * h8 + 8 * g) = pack_bf16x8(tmp);
+        }
+    }
+  } else {
+    float* prow = p.part_dq + ((size_t(b) * p.num_qslots + slot) * BQ + w * 32 + l32) * kD;
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
-        float tmp[8];
+        const int f0 = 32 * fb + 16 * h8 + 8 * g;
+        floatx4 x0, x1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = dqa[fb][8 * h8 + j] * p.scale;
-        *reinterpret_cast<bf16x8*>(row + 32 * fb + 16 * h8 + 8 * g) = pack_bf16x8(tmp);
+        for (int j = 0; j < 4; ++j) {
+          x0[j] = dqa[fb][8 * h8 + j] * p.scale;
+          x1[j] = dqa[fb][8 * h8 + 4 + j] * p.scale;
+        }
+        *reinterpret_cast<floatx4*>(prow + f0) = x0;
+        *reinterpret_cast<floatx4*>(prow + f0 + 4) = x1;
       }
   }
 }
@@ -439,10 +463,32 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 // --------------------------------------------------------------------------
 // Sum the chunk partials of each split key tile (chunk order) -> dK, dV.
 // --------------------------------------------------------------------------
-template <int BK>
+template <int BQ, int BK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
   const int b = blockIdx.x % p.B;
   const int item = blockIdx.x / p.B;
+  if (item >= p.red_len) {
+    // dQ chunks of a split query tile
+    const int32_t* c4 = p.csched + 4 * (item - p.red_len);
+    const int head = c4[0], qt = c4[1], slot0 = c4[2], chunks = c4[3];
+    const PatView pv = pattern_of_head(p.blob, head);
+    const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
+    constexpr int PERQ = BQ * kD;
+    const float* part0 = p.part_dq + (size_t(b) * p.num_qslots + slot0) * PERQ;
+    for (int idx = threadIdx.x * 8; idx < PERQ; idx += 256 * 8) {
+      floatx4 a = floatx4{}, c = floatx4{};
+      for (int ch = 0; ch < chunks; ++ch) {
+        const floatx4* src = reinterpret_cast<const floatx4*>(part0 + size_t(ch) * PERQ + idx);
+        a += src[0];
+        c += src[1];
+      }
+      const int tok = pv.qmap[qt * BQ + idx / kD];
+      if (tok < 0) continue;
+      float tmp[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+      *reinterpret_cast<bf16x8*>(p.dq + (base + tok) * kD + idx % kD) = pack_bf16x8(tmp);
+    }
+    return;
+  }
   const int32_t* it4 = p.rsched + 4 * item;
   const int head = it4[0], kt = it4[1], slot0 = it4[2], chunks = it4[3];
   const PatView pv = pattern_of_head(p.blob, head);
@@ -478,9 +524,14 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t workspace_bytes(int64_t rows, int B, int32_t num_slots, int32_t bk) {
-  return round256(size_t(rows) * sizeof(float)) +
-         size_t(B) * size_t(num_slots) * 2 * size_t(bk) * sa::kD * sizeof(float);
+size_t kv_partial_bytes(int B, int32_t num_slots, int32_t bk) {
+  return round256(size_t(B) * size_t(num_slots) * 2 * size_t(bk) * sa::kD * sizeof(float));
+}
+
+size_t workspace_bytes(int64_t rows, int B, int32_t num_slots, int32_t bk, int32_t num_qslots,
+                       int32_t bq) {
+  return round256(size_t(rows) * sizeof(float)) + kv_partial_bytes(B, num_slots, bk) +
+         size_t(B) * size_t(num_qslots) * size_t(bq) * sa::kD * sizeof(float);
 }
 
 }  // namespace
@@ -495,7 +546,8 @@ extern "C" int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, in
   if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
   if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
   if (d != 64 || dtype != SA_BF16) return SA_EUNSUPPORTED;
-  *bytes = workspace_bytes(int64_t(B) * H * h.n, B, h.num_slots, h.block_k);
+  *bytes = workspace_bytes(int64_t(B) * H * h.n, B, h.num_slots, h.block_k, h.num_qslots,
+                           h.block_q);
   return SA_OK;
 }
 
@@ -520,14 +572,14 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   memcpy(&h, blob_host, sizeof(h));
   const int64_t rows = int64_t(B) * H * li.n;
   if (B == 0) return SA_OK;  // empty batch: pointers may be NULL
-  if (ws_bytes < workspace_bytes(rows, B, h.num_slots, bk)) return SA_ESIZE;
+  if (ws_bytes < workspace_bytes(rows, B, h.num_slots, bk, h.num_qslots, bq)) return SA_ESIZE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return SA_EINVAL;
   const int64_t gq = int64_t(SA_XCDS) * li.fwd_xl_len * B;
   const int64_t gk = int64_t(SA_XCDS) * li.bwd_xl_len * B;
-  const int64_t gr = int64_t(h.red_sched_len) * B;
+  const int64_t gr = int64_t(h.red_sched_len + h.comb_sched_len) * B;
   if (gq > INT32_MAX || gk > INT32_MAX || gr > INT32_MAX) return SA_EUNSUPPORTED;
 
   BwdParams prm;
@@ -535,6 +587,9 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.qsched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
   prm.ksched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
   prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
+  prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
+  prm.num_qslots = h.num_qslots;
+  prm.red_len = h.red_sched_len;
   prm.qxl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
   prm.kxl = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xl_off);
   prm.qxl_len = li.fwd_xl_len;
@@ -555,6 +610,9 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.dsum = static_cast<float*>(workspace);
   prm.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                          round256(size_t(rows) * sizeof(float)));
+  prm.part_dq = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         round256(size_t(rows) * sizeof(float)) +
+                                         kv_partial_bytes(B, h.num_slots, bk));
   prm.scale = sc;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -579,8 +637,12 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else SA_LAUNCH((bwd_dkdv_kernel<128, 64>), gk, 128);
   }
   if ((phases & SA_BWD_REDUCE) && gr > 0) {
-    if (bk == 32) SA_LAUNCH((bwd_reduce_kernel<32>), gr, 256);
-    else SA_LAUNCH((bwd_reduce_kernel<64>), gr, 256);
+    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<32, 32>), gr, 256);
+    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_reduce_kernel<32, 64>), gr, 256);
+    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<64, 32>), gr, 256);
+    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_reduce_kernel<64, 64>), gr, 256);
+    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<128, 32>), gr, 256);
+    else SA_LAUNCH((bwd_reduce_kernel<128, 64>), gr, 256);
   }
 #undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;

@@ -28,24 +28,76 @@
 
 namespace sa {
 
+constexpr float kNegInit = -3.0e38f;  // running-max start: exp2(kNegInit - x) == 0
+constexpr float kMasked = -1.0e30f;   // masked logit in the base-2 domain (float32 path)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
+
 struct FwdParams {
   const uint8_t* blob;
-  const int32_t* sched;  // (head, q-tile) pairs
-  const int32_t* xl;     // per-XCD lists of schedule entries
+  const int32_t* sched;   // (head, q-tile, e0, e1, slot)
+  const int32_t* xl;      // per-XCD lists of schedule entries
+  const int32_t* csched;  // (head, q-tile, slot0, chunks) of split query tiles
   int32_t xl_len;
-  int32_t B, H, n;
+  int32_t B, H, n, num_qslots;
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
+  float* part_o;  // [B, num_qslots, BQ, 64]: unnormalised O of a chunk
+  float* part_m;  // [B, num_qslots, BQ]: running max (base 2)
+  float* part_l;  // [B, num_qslots, BQ]: running sum
   float scale_log2;  // softmax scale * log2(e)
 };
 
-constexpr float kNegInit = -3.0e38f;  // running-max start: exp2(kNegInit - x) == 0
-constexpr float kMasked = -1.0e30f;   // masked logit in the base-2 domain (float32 path)
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
+// Epilogue shared by both element types.  Register r of half g of oacc[fb]
+// holds feature 32*fb + kappa(r, g) of the lane's query row.  Unsplit tiles
+// write O = acc / l and LSE; chunks of split tiles write (acc, m, l).
+template <typename T, int BQ>
+__device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 (&oacc)[2],
+                                             float m_run, float l_run, int tok, size_t base,
+                                             int b, int slot, int row, int g) {
+  const float l_tot = l_run + other_half(l_run);
+  if (slot < 0) {
+    if (tok < 0) return;
+    const float inv = 1.0f / l_tot;
+    T* orow = static_cast<T*>(p.o) + (base + size_t(tok)) * kD;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = oacc[fb][8 * h8 + j] * inv;
+        T* dst = orow + 32 * fb + 16 * h8 + 8 * g;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
+        } else {
+          *reinterpret_cast<floatx4*>(dst) = floatx4{tmp[0], tmp[1], tmp[2], tmp[3]};
+          *reinterpret_cast<floatx4*>(dst + 4) = floatx4{tmp[4], tmp[5], tmp[6], tmp[7]};
+        }
+      }
+    if (g == 0) p.lse[base + tok] = (m_run + log2f(l_tot)) * kLn2;
+    return;
+  }
+  const size_t prow = (size_t(b) * p.num_qslots + slot) * BQ + row;
+  float* po = p.part_o + prow * kD;
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      const int f0 = 32 * fb + 16 * h8 + 8 * g;
+      *reinterpret_cast<floatx4*>(po + f0) =
+          floatx4{oacc[fb][8 * h8], oacc[fb][8 * h8 + 1], oacc[fb][8 * h8 + 2], oacc[fb][8 * h8 + 3]};
+      *reinterpret_cast<floatx4*>(po + f0 + 4) = floatx4{oacc[fb][8 * h8 + 4], oacc[fb][8 * h8 + 5],
+                                                         oacc[fb][8 * h8 + 6], oacc[fb][8 * h8 + 7]};
+    }
+  if (g == 0) {
+    p.part_m[prow] = m_run;
+    p.part_l[prow] = l_tot;
+  }
+}
 
 // --------------------------------------------------------------------------
 // bfloat16 inputs, 32x32x16 bf16 MFMA
@@ -65,7 +117,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int head = p.sched[2 * item], qt = p.sched[2 * item + 1];
+  const int32_t* it5 = p.sched + 5 * item;
+  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const bf16* qg = static_cast<const bf16*>(p.q) + base * kD;
@@ -86,7 +139,6 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
     for (int c = 0; c < 4; ++c) qf[c] = bf16x8{};
   }
 
-  const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
   u32x4 kreg[CPT], vreg[CPT];
   int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
@@ -207,21 +259,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + other_half(l_run);
-  if (tok >= 0) {
-    const float inv = 1.0f / l_tot;
-    bf16* orow = static_cast<bf16*>(p.o) + (base + size_t(tok)) * kD;
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        float tmp[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) tmp[j] = oacc[fb][8 * h8 + j] * inv;
-        *reinterpret_cast<bf16x8*>(orow + 32 * fb + 16 * h8 + 8 * g) = pack_bf16x8(tmp);
-      }
-    if (g == 0) p.lse[base + tok] = (m_run + log2f(l_tot)) * kLn2;
-  }
+  fwd_epilogue<bf16, BQ>(p, oacc, m_run, l_run, tok, base, b, slot, w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------
@@ -243,7 +281,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int head = p.sched[2 * item], qt = p.sched[2 * item + 1];
+  const int32_t* it5 = p.sched + 5 * item;
+  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const float* qg = static_cast<const float*>(p.q) + base * kD;
@@ -258,7 +297,6 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
   for (int c = 0; c < 32; ++c) qf[c] = tok >= 0 ? qg[size_t(tok) * kD + 2 * c + g] : 0.f;
 
-  const int e0 = pv.row_ptr[qt], e1 = pv.row_ptr[qt + 1];
   floatx4 kreg[CPT], vreg[CPT];
   auto gload = [&](int kt) {
 #pragma unroll
@@ -354,25 +392,51 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + other_half(l_run);
-  if (tok >= 0) {
-    const float inv = 1.0f / l_tot;
-    float* orow = static_cast<float*>(p.o) + (base + size_t(tok)) * kD;
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        floatx4 a, c;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = oacc[fb][8 * h8 + j] * inv;
-          c[j] = oacc[fb][8 * h8 + 4 + j] * inv;
-        }
-        float* dst = orow + 32 * fb + 16 * h8 + 8 * g;
-        *reinterpret_cast<floatx4*>(dst) = a;
-        *reinterpret_cast<floatx4*>(dst + 4) = c;
-      }
-    if (g == 0) p.lse[base + tok] = (m_run + log2f(l_tot)) * kLn2;
+  fwd_epilogue<float, BQ>(p, oacc, m_run, l_run, tok, base, b, slot, w * 32 + l32, g);
+}
+
+// --------------------------------------------------------------------------
+// Merge the chunks of split query tiles: with chunk c holding (O_c, m_c, l_c)
+// (unnormalised O, base-2 running max, running sum), m = max_c m_c,
+// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, LSE = (m + log2 l) ln 2.
+// Chunks are summed in chunk order.  8 threads per row (8 features each).
+// --------------------------------------------------------------------------
+template <typename T, int BQ>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p) {
+  const int b = blockIdx.x % p.B;
+  const int item = blockIdx.x / p.B;
+  const int32_t* it4 = p.csched + 4 * item;
+  const int head = it4[0], qt = it4[1], slot0 = it4[2], chunks = it4[3];
+  const PatView pv = pattern_of_head(p.blob, head);
+  const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
+  for (int t = threadIdx.x; t < BQ * 8; t += 256) {
+    const int row = t >> 3, part = t & 7;
+    const int tok = pv.qmap[qt * BQ + row];
+    if (tok < 0) continue;
+    const size_t r0 = (size_t(b) * p.num_qslots + slot0) * BQ + row;
+    float m = -INFINITY;
+    for (int c = 0; c < chunks; ++c) m = fmaxf(m, p.part_m[r0 + size_t(c) * BQ]);
+    float l = 0.f;
+    floatx4 a = floatx4{}, a2 = floatx4{};
+    for (int c = 0; c < chunks; ++c) {
+      const size_t rc = r0 + size_t(c) * BQ;
+      const float wgt = fast_exp2(p.part_m[rc] - m);
+      l += wgt * p.part_l[rc];
+      const floatx4* src = reinterpret_cast<const floatx4*>(p.part_o + rc * kD + 8 * part);
+      a += wgt * src[0];
+      a2 += wgt * src[1];
+    }
+    const float inv = 1.0f / l;
+    float tmp[8] = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv,
+                    a2[0] * inv, a2[1] * inv, a2[2] * inv, a2[3] * inv};
+    T* dst = static_cast<T*>(p.o) + (base + size_t(tok)) * kD + 8 * part;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
+    } else {
+      *reinterpret_cast<floatx4*>(dst) = floatx4{tmp[0], tmp[1], tmp[2], tmp[3]};
+      *reinterpret_cast<floatx4*>(dst + 4) = floatx4{tmp[4], tmp[5], tmp[6], tmp[7]};
+    }
+    if (part == 0) p.lse[base + tok] = (m + log2f(l)) * kLn2;
   }
 }
 
@@ -383,53 +447,121 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 // --------------------------------------------------------------------------
 #include "abi_common.hpp"
 
-extern "C" int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d,
-                               int dtype, const void* q, const void* k, const void* v, void* o,
-                               float* lse, float scale, void* stream) {
+namespace {
+
+size_t fwd_workspace_bytes(int B, int32_t num_qslots, int32_t bq) {
+  const size_t rows = size_t(B) * size_t(num_qslots) * size_t(bq);
+  const size_t o = (rows * sa::kD * sizeof(float) + 255) & ~size_t(255);
+  const size_t ml = (rows * sizeof(float) + 255) & ~size_t(255);
+  return o + 2 * ml;
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_fwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
+                                         size_t* bytes) {
   using namespace sa;
+  if (!bytes || !blob_host) return SA_EINVAL;
+  sa_blob_header h;
+  memcpy(&h, blob_host, sizeof(h));
+  if (h.magic != SA_BLOB_MAGIC || h.version != SA_BLOB_VERSION) return SA_EINVAL;
+  if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
+  if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
+  if (d != 64) return SA_EUNSUPPORTED;
+  *bytes = fwd_workspace_bytes(B, h.num_qslots, h.block_q);
+  return SA_OK;
+}
+
+extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_dev, int B, int H,
+                                      int d, int dtype, const void* q, const void* k,
+                                      const void* v, void* o, float* lse, void* workspace,
+                                      size_t ws_bytes, float scale, unsigned phases,
+                                      void* stream) {
+  using namespace sa;
+  if (phases == 0 || (phases & ~unsigned(SA_FWD_ALL)) != 0) return SA_EINVAL;
   LaunchInfo li;
   int rc = validate_common(blob_host, blob_dev, B, H, d, dtype, &li);
   if (rc != SA_OK) return rc;
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
+  sa_blob_header h;
+  memcpy(&h, blob_host, sizeof(h));
+  const int bq = li.block_q, bk = li.block_k;
+  const bool shape_ok = dtype == SA_BF16 ? (bk == 32 || bk == 64) : (bk == 32);
+  if (!shape_ok) return SA_EUNSUPPORTED;
   if (B == 0 || li.fwd_xl_len == 0) return SA_OK;  // empty batch: pointers may be NULL
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  const size_t need = fwd_workspace_bytes(B, h.num_qslots, bq);
+  if (ws_bytes < need) return SA_ESIZE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (need > 0 && !aligned16(workspace)))
     return SA_EINVAL;
   const int64_t grid = int64_t(SA_XCDS) * li.fwd_xl_len * B;
-  if (grid > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t cgrid = int64_t(h.comb_sched_len) * B;
+  if (grid > INT32_MAX || cgrid > INT32_MAX) return SA_EUNSUPPORTED;
 
   FwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
   prm.sched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
   prm.xl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
+  prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
   prm.xl_len = li.fwd_xl_len;
   prm.B = B;
   prm.H = H;
   prm.n = int32_t(li.n);
+  prm.num_qslots = h.num_qslots;
   prm.q = q;
   prm.k = k;
   prm.v = v;
   prm.o = o;
   prm.lse = lse;
+  {
+    const size_t rows = size_t(B) * size_t(h.num_qslots) * size_t(bq);
+    const size_t ob = (rows * kD * sizeof(float) + 255) & ~size_t(255);
+    const size_t mb = (rows * sizeof(float) + 255) & ~size_t(255);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    prm.part_o = need ? reinterpret_cast<float*>(ws) : nullptr;
+    prm.part_m = need ? reinterpret_cast<float*>(ws + ob) : nullptr;
+    prm.part_l = need ? reinterpret_cast<float*>(ws + ob + mb) : nullptr;
+  }
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const int bq = li.block_q, bk = li.block_k;
-  const dim3 grd{unsigned(grid), 1u, 1u};
-  if (dtype == SA_BF16) {
-    if (bq == 32 && bk == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, 32>), grd, dim3(64), 0, st, prm);
-    else if (bq == 32 && bk == 64) hipLaunchKernelGGL((fwd_bf16_kernel<32, 64>), grd, dim3(64), 0, st, prm);
-    else if (bq == 64 && bk == 32) hipLaunchKernelGGL((fwd_bf16_kernel<64, 32>), grd, dim3(128), 0, st, prm);
-    else if (bq == 64 && bk == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), grd, dim3(128), 0, st, prm);
-    else if (bq == 128 && bk == 32) hipLaunchKernelGGL((fwd_bf16_kernel<128, 32>), grd, dim3(256), 0, st, prm);
-    else if (bq == 128 && bk == 64) hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), grd, dim3(256), 0, st, prm);
-    else return SA_EUNSUPPORTED;
-  } else {
-    if (bq == 32 && bk == 32) hipLaunchKernelGGL((fwd_f32_kernel<32, 32>), grd, dim3(64), 0, st, prm);
-    else if (bq == 64 && bk == 32) hipLaunchKernelGGL((fwd_f32_kernel<64, 32>), grd, dim3(128), 0, st, prm);
-    else if (bq == 128 && bk == 32) hipLaunchKernelGGL((fwd_f32_kernel<128, 32>), grd, dim3(256), 0, st, prm);
-    else return SA_EUNSUPPORTED;
+#define SA_LAUNCH(kern, g, threads) \
+  hipLaunchKernelGGL(kern, dim3(unsigned(g)), dim3(threads), 0, st, prm)
+  if (phases & SA_FWD_MAIN) {
+    if (dtype == SA_BF16) {
+      if (bq == 32 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<32, 32>), grid, 64);
+      else if (bq == 32 && bk == 64) SA_LAUNCH((fwd_bf16_kernel<32, 64>), grid, 64);
+      else if (bq == 64 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<64, 32>), grid, 128);
+      else if (bq == 64 && bk == 64) SA_LAUNCH((fwd_bf16_kernel<64, 64>), grid, 128);
+      else if (bq == 128 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<128, 32>), grid, 256);
+      else SA_LAUNCH((fwd_bf16_kernel<128, 64>), grid, 256);
+    } else {
+      if (bq == 32) SA_LAUNCH((fwd_f32_kernel<32, 32>), grid, 64);
+      else if (bq == 64) SA_LAUNCH((fwd_f32_kernel<64, 32>), grid, 128);
+      else SA_LAUNCH((fwd_f32_kernel<128, 32>), grid, 256);
+    }
   }
+  if ((phases & SA_FWD_COMBINE) && cgrid > 0) {
+    if (dtype == SA_BF16) {
+      if (bq == 32) SA_LAUNCH((fwd_combine_kernel<bf16, 32>), cgrid, 256);
+      else if (bq == 64) SA_LAUNCH((fwd_combine_kernel<bf16, 64>), cgrid, 256);
+      else SA_LAUNCH((fwd_combine_kernel<bf16, 128>), cgrid, 256);
+    } else {
+      if (bq == 32) SA_LAUNCH((fwd_combine_kernel<float, 32>), cgrid, 256);
+      else if (bq == 64) SA_LAUNCH((fwd_combine_kernel<float, 64>), cgrid, 256);
+      else SA_LAUNCH((fwd_combine_kernel<float, 128>), cgrid, 256);
+    }
+  }
+#undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;
+}
+
+extern "C" int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d,
+                               int dtype, const void* q, const void* k, const void* v, void* o,
+                               float* lse, void* workspace, size_t ws_bytes, float scale,
+                               void* stream) {
+  return sparse_attn_fwd_phases(blob_host, blob_dev, B, H, d, dtype, q, k, v, o, lse, workspace,
+                                ws_bytes, scale, SA_FWD_ALL, stream);
 }

@@ -289,6 +289,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   if (desc->num_heads < 1 || desc->num_heads > kMaxHeads || !desc->heads) return SA_EINVAL;
   if (!valid_tile(desc->block_q) || !valid_tile(desc->block_k)) return SA_EUNSUPPORTED;
   if (desc->flags & ~SA_SELF_IF_EMPTY) return SA_EINVAL;
+  if (desc->split_keys < 0 || desc->split_rows < 0) return SA_EINVAL;
   const bool self_if_empty = (desc->flags & SA_SELF_IF_EMPTY) != 0;
   const int32_t n = int32_t(desc->n);
   const int32_t bq = desc->block_q, bk = desc->block_k;
@@ -318,17 +319,39 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   }
 
   std::vector<SchedItem> fwd_items, bwd_items;
-  std::vector<int32_t> red_sched;  // (head, k-tile, first slot, chunks)
-  int32_t num_slots = 0;
-  const int32_t cap = std::max<int32_t>(1, SA_SPLIT_ROWS / bq);  // q-tiles per dK/dV chunk
+  std::vector<int32_t> red_sched;   // (head, k-tile, first slot, chunks)
+  std::vector<int32_t> comb_sched;  // (head, q-tile, first slot, chunks)
+  int32_t num_slots = 0, num_qslots = 0;
+  const int32_t split_rows = desc->split_rows > 0 ? desc->split_rows : SA_SPLIT_ROWS;
+  const int32_t split_keys = desc->split_keys > 0 ? desc->split_keys : SA_SPLIT_KEYS;
+  const int32_t cap = std::max<int32_t>(1, split_rows / bq);   // q-tiles per dK/dV chunk
+  const int32_t qcap = std::max<int32_t>(1, split_keys / bk);  // k-tiles per forward / dQ chunk
   int64_t pairs_all = 0, tiles_all = 0;
   for (int32_t h = 0; h < desc->num_heads; ++h) {
     const Pattern& P = pats[head_pat[h]];
     pairs_all += P.pairs;
     tiles_all += int64_t(P.col.size());
     for (int32_t qt = 0; qt < nqt; ++qt) {
-      const int32_t w = P.row_ptr[qt + 1] - P.row_ptr[qt];
-      if (w > 0) fwd_items.push_back({h, qt, w});
+      const int32_t r0 = P.row_ptr[qt], r1 = P.row_ptr[qt + 1], len = r1 - r0;
+      if (len == 0) continue;
+      if (len <= qcap) {
+        SchedItem it{h, qt, len};
+        it.e0 = r0;
+        it.e1 = r1;
+        fwd_items.push_back(it);
+        continue;
+      }
+      const int32_t chunks = (len + qcap - 1) / qcap;
+      comb_sched.insert(comb_sched.end(), {h, qt, num_qslots, chunks});
+      for (int32_t c = 0; c < chunks; ++c) {
+        SchedItem it{h, qt, 0};
+        it.e0 = r0 + int32_t(int64_t(len) * c / chunks);
+        it.e1 = r0 + int32_t(int64_t(len) * (c + 1) / chunks);
+        it.work = it.e1 - it.e0;
+        it.slot = num_qslots + c;
+        fwd_items.push_back(it);
+      }
+      num_qslots += chunks;
     }
     for (int32_t kt = 0; kt < nkt; ++kt) {
       if (kt * bk >= n) continue;  // all padding keys
@@ -354,7 +377,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       num_slots += chunks;
     }
   }
-  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items, 2);
+  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items, 5);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items, 5);
   std::vector<int32_t> fwd_xl, bwd_xl;
   const int32_t fwd_xl_len = xcd_lists(fwd_items, fwd_xl);
@@ -373,6 +396,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwd_sched_off = w.put(bwd_sched);
     hdr.red_sched_off = w.put(red_sched);
     hdr.fwd_xl_off = w.put(fwd_xl);
+    hdr.comb_sched_off = w.put(comb_sched);
     hdr.bwd_xl_off = w.put(bwd_xl);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
@@ -427,6 +451,10 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.red_sched_len = int32_t(red_sched.size() / 4);
     hdr.num_slots = num_slots;
     hdr.fwd_xl_len = fwd_xl_len;
+    hdr.comb_sched_len = int32_t(comb_sched.size() / 4);
+    hdr.num_qslots = num_qslots;
+    hdr.split_keys = split_keys;
+    hdr.split_rows = split_rows;
     hdr.bwd_xl_len = bwd_xl_len;
     hdr.pairs_all_heads = pairs_all;
     hdr.tiles_all_heads = tiles_all;
@@ -469,7 +497,8 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
     return SA_EINVAL;
   if (!in_blob(h.head_pattern_off, 4 * int64_t(h.num_heads), total) ||
       !in_blob(h.pattern_off, int64_t(sizeof(sa_pattern_rec)) * h.num_patterns, total) ||
-      !in_blob(h.fwd_sched_off, 8 * int64_t(h.fwd_sched_len), total) ||
+      !in_blob(h.fwd_sched_off, 20 * int64_t(h.fwd_sched_len), total) ||
+      !in_blob(h.comb_sched_off, 16 * int64_t(h.comb_sched_len), total) || h.num_qslots < 0 ||
       !in_blob(h.bwd_sched_off, 20 * int64_t(h.bwd_sched_len), total) ||
       !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0 ||
       !in_blob(h.fwd_xl_off, 4 * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||

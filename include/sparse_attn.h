@@ -82,6 +82,8 @@ typedef struct {
   int32_t num_heads;             /* 1 .. 4096 */
   const sa_head_pattern* heads;  /* num_heads entries, host memory */
   uint32_t flags;                /* SA_SELF_IF_EMPTY or 0 */
+  int32_t split_keys;            /* query-tile chunk cap in keys; 0 = SA_SPLIT_KEYS */
+  int32_t split_rows;            /* key-tile chunk cap in query rows; 0 = SA_SPLIT_ROWS */
 } sa_layout_desc;
 
 /* ---------------------------------------------------------------------------
@@ -110,11 +112,16 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 3u
-/* Key tiles read by more than this many query rows are split into chunks for
- * the dK/dV pass (each chunk a workgroup); their partial sums are reduced in a
- * fixed order. */
+#define SA_BLOB_VERSION 5u
+/* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
+ * by more than split_rows query rows are split into chunks of at most that
+ * many rows (rounded down to whole query tiles, at least one) for the dK/dV
+ * pass, each chunk a workgroup; their partial sums are reduced in a fixed
+ * order.  Query tiles that read more than split_keys keys are split the same
+ * way for the forward and dQ passes; chunk results are merged in a fixed
+ * order.  A cap of at least n disables splitting. */
 #define SA_SPLIT_ROWS 1536
+#define SA_SPLIT_KEYS 1024
 /* Number of accelerator complex dies (XCDs, each with its own L2) that
  * workgroups are dealt to round-robin on MI355X. */
 #define SA_XCDS 8
@@ -150,7 +157,8 @@ typedef struct {
   int64_t total_bytes;
   int64_t head_pattern_off; /* int32[num_heads]: pattern index of each head */
   int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
-  int64_t fwd_sched_off;    /* int32[2 * fwd_sched_len]: (head, q-tile), heaviest first */
+  int64_t fwd_sched_off;    /* int32[5 * fwd_sched_len]: (head, q-tile, first CSR entry,
+                               end CSR entry, partial slot or -1), heaviest first */
   int64_t bwd_sched_off;    /* int32[5 * bwd_sched_len]: (head, k-tile, first CSC entry,
                                end CSC entry, partial slot or -1), heaviest first */
   int32_t fwd_sched_len, bwd_sched_len;
@@ -166,6 +174,10 @@ typedef struct {
   int64_t fwd_xl_off;       /* int32[SA_XCDS * fwd_xl_len], indices into fwd_sched */
   int64_t bwd_xl_off;       /* int32[SA_XCDS * bwd_xl_len], indices into bwd_sched */
   int32_t fwd_xl_len, bwd_xl_len;
+  int64_t comb_sched_off;   /* int32[4 * comb_sched_len]: (head, q-tile, first slot, chunks) */
+  int32_t comb_sched_len;
+  int32_t num_qslots;       /* query-tile partial slots per batch element */
+  int32_t split_keys, split_rows; /* chunk caps the schedules were built with */
   int64_t pairs_all_heads;  /* sum of pairs over the heads (one batch element) */
   int64_t tiles_all_heads;  /* sum of active tiles over the heads */
 } sa_blob_header;
@@ -178,12 +190,30 @@ int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_byte
 /* Check a blob's header and internal offsets (host). */
 int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes);
 
+/* Bytes of device workspace sparse_attn_fwd needs for these sizes (0 when
+ * the layout splits no query tile; the workspace may then be NULL). */
+int sparse_attn_fwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
+                              size_t* bytes);
+
 /* Forward (report sections 3.5 and 3.4): o [B,H,n,d] in dtype, lse [B,H,n]
- * float32.  scale <= 0 selects 1/sqrt(d).  B == 0 is a valid no-op (the
- * tensor pointers may then be NULL). */
+ * float32.  scale <= 0 selects 1/sqrt(d).  workspace: ws_bytes >= the size
+ * returned by sparse_attn_fwd_workspace, 16-byte aligned, contents on entry
+ * irrelevant (it holds the partial results of split query tiles).  B == 0 is
+ * a valid no-op (the tensor pointers may then be NULL). */
 int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
                     const void* q, const void* k, const void* v, void* o, float* lse,
-                    float scale, void* stream);
+                    void* workspace, size_t ws_bytes, float scale, void* stream);
+
+/* The forward as two separately launchable phases (same arguments, one
+ * stream, in order): SA_FWD_MAIN runs the block-sparse kernel (unsplit query
+ * tiles write O and LSE, chunks of split tiles write partial results to the
+ * workspace); SA_FWD_COMBINE merges the chunks of split tiles in chunk order
+ * and writes their O and LSE.  sparse_attn_fwd runs SA_FWD_ALL. */
+enum { SA_FWD_MAIN = 1, SA_FWD_COMBINE = 2, SA_FWD_ALL = 3 };
+int sparse_attn_fwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
+                           int dtype, const void* q, const void* k, const void* v, void* o,
+                           float* lse, void* workspace, size_t ws_bytes, float scale,
+                           unsigned phases, void* stream);
 
 /* Bytes of device workspace sparse_attn_bwd needs for these sizes. */
 int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
@@ -202,11 +232,13 @@ int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, i
 
 /* The backward as three separately launchable phases, for callers that
  * interleave other work between them or time them one by one:
- *   SA_BWD_DQ      per query tile: D_i = dO_i . O_i (kept in the workspace)
- *                  and dQ, written in dtype;
+ *   SA_BWD_DQ      per query tile (long tiles in chunks): D_i = dO_i . O_i
+ *                  (kept in the workspace) and dQ, written in dtype, or
+ *                  float32 partial sums of split tiles (workspace);
  *   SA_BWD_DKDV    per key tile (long tiles in chunks): dK, dV written in
  *                  dtype, or float32 partial sums of split tiles (workspace);
- *   SA_BWD_REDUCE  sums the partials of split key tiles in a fixed order.
+ *   SA_BWD_REDUCE  sums the partials of split query and key tiles in a fixed
+ *                  order and writes their dQ, dK, dV.
  * Phases must run in this order on one stream with the same arguments and
  * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL).
  * Every phase is deterministic (no atomics). */

@@ -36,6 +36,10 @@ SMALL = [
     ("degenerate", 1, 130, 64, 64, [HeadPattern("local", 1000), HeadPattern("stride", 1000),
                                     HeadPattern("summary", 8, 8, 0), HeadPattern("stride", 1)]),
     ("single_row", 1, 1, 64, 64, [HeadPattern("local", 4), HeadPattern("summary", 4, 2, 0)]),
+    # rows reading more than 1024 keys: forward / dQ chunks, combine and reduce launches
+    ("split_k32", 2, 1500, 64, 32, [HeadPattern("local", 1400), HeadPattern("stride", 1)]),
+    ("split_q128_k64", 1, 2200, 128, 64, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
+                                          HeadPattern("sameblock", 2048)]),
 ]
 
 
@@ -70,6 +74,14 @@ def test_fp32_forward_small_ragged():
     lay = Layout(200, heads, 32, 32)
     inp = W.make_inputs(1, 3, 200, 64, seed=5, dtype="fp32")
     _check_dense(lay, heads, 1, 200, inp, backward=False, fp32=True)
+
+
+def test_fp32_forward_split_rows():
+    heads = [HeadPattern("local", 1100), HeadPattern("stride", 2)]
+    lay = Layout(1100, heads, 64, 32)
+    assert lay.header.comb_sched_len > 0
+    inp = W.make_inputs(1, 2, 1100, 64, seed=6, dtype="fp32")
+    _check_dense(lay, heads, 1, 1100, inp, backward=False, fp32=True)
 
 
 def test_workload_strided_n1024_fp32_full():

@@ -123,15 +123,16 @@ def test_schedules_cover_every_tile_heaviest_first():
     h = lay.header
     fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
     fwork, bwork = [], []
-    for head, qt in fs:
+    for head, qt, e0, e1, slot in fs:
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
-        fwork.append(a["row_ptr"][qt + 1] - a["row_ptr"][qt])
+        assert (e0, e1, slot) == (a["row_ptr"][qt], a["row_ptr"][qt + 1], -1)  # no split at n=1000
+        fwork.append(e1 - e0)
     for head, kt, e0, e1, slot in bs:
         bwork.append(e1 - e0)
     assert all(w > 0 for w in fwork)
     assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
-    assert sorted(map(tuple, fs.tolist())) == [(hh, q) for hh in range(2) for q in range(h.nqt)
-                                               if q * 64 < 1000]
+    assert sorted(tuple(r[:2]) for r in fs.tolist()) == [(hh, q) for hh in range(2)
+                                                        for q in range(h.nqt) if q * 64 < 1000]
     assert sorted({(int(r[0]), int(r[1])) for r in bs}) == [(hh, k) for hh in range(2)
                                                            for k in range(h.nkt) if k * 64 < 1000]
 
@@ -150,7 +151,7 @@ def test_xcd_lists_cover_every_schedule_entry_once(n, bq, bk, heads):
         assert xl.shape[0] == bd.SA_XCDS
         flat = xl[xl >= 0]
         assert sorted(flat.tolist()) == list(range(len(sched)))
-        keys = [tuple(sched[i][:2]) + ((int(sched[i][2]),) if which == "bwd" else ()) for i in range(len(sched))]
+        keys = [tuple(int(x) for x in sched[i][:3]) for i in range(len(sched))]
         natural = sorted(range(len(sched)), key=lambda i: keys[i])
         rank = {i: r for r, i in enumerate(natural)}
         prev_max = -1
@@ -174,7 +175,8 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
     """Each key tile's CSC list is covered exactly once, in chunks of at most the split cap."""
     lay = Layout(n, heads, bq, bk)
     h = lay.header
-    cap = max(1, 1536 // bq)
+    assert h.split_rows == 1536
+    cap = max(1, h.split_rows // bq)
     bs, rs = lay.bwd_schedule(), lay.reduce_schedule()
     slots = sorted(int(r[4]) for r in bs if r[4] >= 0)
     assert slots == list(range(h.num_slots))
@@ -196,6 +198,71 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
                 assert [r[2] for r in rows] == list(range(s0, s0 + nch))
     if n == 12288:
         assert h.red_sched_len > 0 and h.num_slots > h.red_sched_len
+
+
+@pytest.mark.parametrize("n,bq,bk,heads", [
+    (12288, 128, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
+                      HeadPattern("summary", 128, 32, 3)]),
+    (12288, 64, 64, [HeadPattern("local", 128), HeadPattern("stride", 128)]),
+    (5000, 32, 32, [HeadPattern("summary", 64, 4, 1), HeadPattern("local", 3000)]),
+    (3072, 64, 64, [HeadPattern("local", 64), HeadPattern("stride", 64)]),
+])
+def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
+    """Each query tile's CSR list is covered exactly once by forward / dQ items, in
+    contiguous chunks of at most 1024 keys; split tiles own consecutive slots that
+    the combine schedule lists."""
+    lay = Layout(n, heads, bq, bk)
+    h = lay.header
+    assert h.split_keys == 1024
+    qcap = max(1, h.split_keys // bk)
+    fs, cs = lay.fwd_schedule(), lay.combine_schedule()
+    slots = sorted(int(r[4]) for r in fs if r[4] >= 0)
+    assert slots == list(range(h.num_qslots))
+    comb = {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in cs}
+    assert len(comb) == len(cs) == h.comb_sched_len
+    for head in range(len(heads)):
+        a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
+        for qt in range(h.nqt):
+            r0, r1 = int(a["row_ptr"][qt]), int(a["row_ptr"][qt + 1])
+            rows = sorted((int(r[2]), int(r[3]), int(r[4])) for r in fs if r[0] == head and r[1] == qt)
+            if r1 == r0:
+                assert rows == [] and (head, qt) not in comb
+                continue
+            assert rows[0][0] == r0 and rows[-1][1] == r1
+            assert all(x[1] == y[0] for x, y in zip(rows, rows[1:]))
+            assert all(0 < e1 - e0 <= qcap for e0, e1, _ in rows)
+            if r1 - r0 <= qcap:
+                assert rows == [(r0, r1, -1)] and (head, qt) not in comb
+            else:
+                s0, nch = comb[(head, qt)]
+                assert nch == -(-(r1 - r0) // qcap)
+                assert [r[2] for r in rows] == list(range(s0, s0 + nch))
+    if n == 12288:
+        # summary heads read up to 3072 keys per row; strided heads stay within one class
+        assert (h.comb_sched_len > 0) == any(p.kind == "summary" for p in heads)
+
+
+@pytest.mark.parametrize("split_keys,split_rows", [(256, 320), (96, 64), (1 << 30, 1 << 30)])
+def test_chunk_caps_are_layout_parameters(split_keys, split_rows):
+    """Caller-chosen caps: every chunk within them (at least one tile), and caps at
+    least n split nothing."""
+    heads = [HeadPattern("summary", 64, 16, 0), HeadPattern("local", 700), HeadPattern("stride", 3)]
+    n, bq, bk = 900, 64, 32
+    lay = Layout(n, heads, bq, bk, split_keys=split_keys, split_rows=split_rows)
+    h = lay.header
+    assert (h.split_keys, h.split_rows) == (split_keys, split_rows)
+    qcap, cap = max(1, split_keys // bk), max(1, split_rows // bq)
+    fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
+    assert all(0 < r[3] - r[2] <= qcap for r in fs)
+    assert all(0 <= r[3] - r[2] <= cap for r in bs)  # unread key tiles: zero dK, dV
+    if split_keys >= n:
+        assert h.comb_sched_len == h.num_qslots == 0 and h.red_sched_len == h.num_slots == 0
+    else:
+        assert h.comb_sched_len > 0 and h.red_sched_len > 0
+    ref = Layout(n, heads, bq, bk)
+    for i in range(ref.num_patterns):  # the caps change schedules only
+        for key, arr in ref.pattern_arrays(i).items():
+            np.testing.assert_array_equal(lay.pattern_arrays(i)[key], arr)
 
 
 def test_padding_overhead_closed_form_12288():
@@ -239,6 +306,15 @@ def _raw_layout(n, heads, bq=64, bk=64, flags=1):
 def test_layout_rejects_bad_descriptors(n, heads, bq, bk, flags, expect):
     rc, _ = _raw_layout(n, [bd.CHeadPattern(*h) for h in heads], bq, bk, flags)
     assert rc == expect
+
+
+def test_layout_rejects_negative_chunk_caps():
+    lib = bd.load_library()
+    arr = (bd.CHeadPattern * 1)(bd.CHeadPattern(0, 8, 0, 0))
+    size = ctypes.c_size_t(0)
+    for ks, rs in ((-1, 0), (0, -64)):
+        desc = bd.CLayoutDesc(64, 64, 64, 1, arr, 1, ks, rs)
+        assert lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)) == bd.SA_EINVAL
 
 
 def test_layout_without_self_if_empty_when_no_row_is_empty():
@@ -322,7 +398,11 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     fake = 1 << 20  # aligned non-null device-looking address; never dereferenced on these paths
     f = lambda **kw: lib.sparse_attn_fwd(kw.get("blob", hb), kw.get("dev", fake), kw.get("B", 1),
                                          kw.get("H", 2), kw.get("d", 64), kw.get("dt", 0), fake,
-                                         fake, fake, kw.get("o", fake), fake, kw.get("scale", 0.0), None)
+                                         fake, fake, kw.get("o", fake), fake, kw.get("ws", fake),
+                                         kw.get("wsb", 1 << 30), kw.get("scale", 0.0), None)
+    fp = lambda ph: lib.sparse_attn_fwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake,
+                                               fake, 1 << 30, 0.0, ph, None)
+    assert fp(0) == bd.SA_EINVAL and fp(4) == bd.SA_EINVAL
     assert f(blob=None) == bd.SA_EINVAL
     assert f(H=3) == bd.SA_EINVAL
     assert f(B=-1) == bd.SA_EINVAL
@@ -333,6 +413,19 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert f(dev=fake + 8) == bd.SA_EINVAL
     assert f(scale=float("nan")) == bd.SA_EINVAL
     assert f(B=0) == bd.SA_OK  # empty batch: nothing to do
+    size = ctypes.c_size_t(1)
+    assert lib.sparse_attn_fwd_workspace(hb, 2, 2, 64, 0, ctypes.byref(size)) == 0
+    assert size.value == 0  # no query tile is split at n=128
+    assert lib.sparse_attn_fwd_workspace(hb, 2, 2, 128, 0, ctypes.byref(size)) == bd.SA_EUNSUPPORTED
+    big = Layout(12288, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0)], 64, 64)
+    assert big.header.num_qslots > 0
+    assert lib.sparse_attn_fwd_workspace(big.blob.ctypes.data, 3, 2, 64, 0, ctypes.byref(size)) == 0
+    rows = 3 * big.header.num_qslots * 64
+    rnd = lambda x: -(-x // 256) * 256
+    assert size.value == rnd(rows * 64 * 4) + 2 * rnd(rows * 4)
+    hbig = big.blob.ctypes.data
+    assert lib.sparse_attn_fwd(hbig, fake, 3, 2, 64, 0, fake, fake, fake, fake, fake, fake,
+                               size.value - 1, 0.0, None) == bd.SA_ESIZE
     size = ctypes.c_size_t(0)
     assert lib.sparse_attn_bwd_workspace(hb, 2, 2, 64, 0, ctypes.byref(size)) == 0
     assert lay.header.num_slots == 0
