@@ -11,7 +11,13 @@ resident in HBM:
   fixed_n12288    B=2, H=8, l=128, c=32, alternating same-block / summary heads
   strided_n12288  B=1, H=16, l=128, alternating local / stride heads,
                   shared period-128 sinusoid in Q and K
-Prints one JSON line.  ``--gpus`` above 1 exits: this build measures one GPU.
+Timing: W untimed warm-up steps; then K steps between two HIP events with
+nothing else recorded (ms_per_step, value); then K more steps with an event
+pair around every launch for the per-kernel table and the roofline entry of
+the longest kernel (those intervals include the cost of an event, reported
+as event_overhead_us).
+
+Prints one JSON line.  ``--gpus`` above 1 exits: the path runs on one GPU.
 """
 
 from __future__ import annotations
@@ -51,8 +57,8 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
         return 2 * D * pairs, rows * (5 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
     if label == "bwd_dkdv":
         return 6 * D * pairs, rows * (6 * D * 2 + 8)             # Q,K,V,dO read, dK,dV write; LSE, D
-    if label in ("fwd_combine", "bwd_reduce"):
-        return 0, 0
+    if label in ("fwd_merge", "bwd_merge"):
+        return 0, 0  # merges of split tiles: no useful FLOPs of their own
     raise ValueError(label)
 
 
@@ -133,8 +139,8 @@ def cpu_baseline(workloads, inputs, seconds: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,15 +172,18 @@ def main():
         fws = torch.empty(max(1, bd.fwd_workspace_bytes(lay, w.B, w.H, dtype=dt)), dtype=torch.uint8,
                           device=dev)
         pairs = lay.pairs_per_batch() * w.B
+        split_q, split_k = lay.header.comb_sched_len > 0, lay.header.red_sched_len > 0
         calls = []
-        for label, ph in (("fwd", bd.SA_FWD_MAIN), ("fwd_combine", bd.SA_FWD_COMBINE)):
-            if label == "fwd_combine" and lay.header.comb_sched_len == 0:
+        for label, ph in (("fwd", bd.SA_FWD_MAIN), ("fwd_merge", bd.SA_FWD_MERGE)):
+            if label == "fwd_merge" and not split_q:
                 continue
             calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, fws=fws, ph=ph:
                           bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws, phases=ph)))
         if w.backward:
             for label, ph in (("bwd_dq", bd.SA_BWD_DQ), ("bwd_dkdv", bd.SA_BWD_DKDV),
-                              ("bwd_reduce", bd.SA_BWD_REDUCE)):
+                              ("bwd_merge", bd.SA_BWD_MERGE)):
+                if label == "bwd_merge" and not (split_q or split_k):
+                    continue
                 calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, do=do, ws=ws, grads=grads, ph=ph:
                               bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads, phases=ph)))
         useful = (12 if w.backward else 4) * D * pairs
@@ -196,18 +205,32 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Timed region: K whole steps between two events, nothing recorded inside
+    # (each event costs the GPU about 5 us, which would inflate the step).
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(flat) + 1)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for s in range(K):
-        step(evs[s])
+        step()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / K
+
+    # Per-kernel breakdown: K more steps with an event before and after every
+    # launch, on the stream the library launches on (torch's current stream).
+    # These intervals include the event cost; it is measured right after, with
+    # back-to-back events queued behind the last launches.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(flat) + 1)] for _ in range(K)]
+    for s in range(K):
+        step(evs[s])
+    b2b = [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+    for e in b2b:
+        e.record()
+    torch.cuda.synchronize()
     per_call_ms = [sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)) / K for i in range(len(flat))]
+    event_us = 1000 * b2b[0].elapsed_time(b2b[-1]) / (len(b2b) - 1)
 
     useful = sum(r["useful"] for r in runs)
     value = useful / (ms_per_step * 1e-3) / 1e12
@@ -230,7 +253,7 @@ def main():
     dom = max(kernels, key=lambda k: k["ms"])
     roof = roofline_entry(dom["flops"], dom["bytes"], dom["ms"] * 1e-3)
     roof.update({"traffic": None, "kernel": f"{dom['kernel']} ({dom['workload']})",
-                 "launch_us": round(dom["ms"] * 1e3, 2)})
+                 "launch_us": round(dom["ms"] * 1e3, 2), "event_overhead_us": round(event_us, 2)})
     for k in kernels:
         k["ms"] = round(k["ms"], 4)
 

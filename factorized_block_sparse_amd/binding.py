@@ -32,8 +32,9 @@ EXPORTED = (
     "sparse_attn_fwd", "sparse_attn_fwd_phases", "sparse_attn_bwd_workspace",
     "sparse_attn_bwd", "sparse_attn_bwd_phases", "sparse_attn_strerror",
 )
-SA_FWD_MAIN, SA_FWD_COMBINE, SA_FWD_ALL = 1, 2, 3
-SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_REDUCE, SA_BWD_ALL = 1, 2, 4, 7
+SA_FWD_MAIN, SA_FWD_MERGE, SA_FWD_ALL = 1, 2, 3
+SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_MERGE, SA_BWD_ALL = 1, 2, 4, 7
+SA_SCHED_FIELDS = 8
 
 
 class CHeadPattern(ctypes.Structure):
@@ -218,16 +219,19 @@ class Layout:
         }
 
     def fwd_schedule(self) -> np.ndarray:
-        """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot or -1)."""
-        return self._arr(self.header.fwd_sched_off, 5 * self.header.fwd_sched_len, np.int32).reshape(-1, 5)
+        """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot, merge group,
+        first slot of the group, chunks of the group); -1 / 1 for unsplit tiles."""
+        return self._arr(self.header.fwd_sched_off, SA_SCHED_FIELDS * self.header.fwd_sched_len,
+                         np.int32).reshape(-1, SA_SCHED_FIELDS)
 
     def combine_schedule(self) -> np.ndarray:
         """Rows (head, q-tile, first partial slot, chunks) of the split query tiles."""
         return self._arr(self.header.comb_sched_off, 4 * self.header.comb_sched_len, np.int32).reshape(-1, 4)
 
     def bwd_schedule(self) -> np.ndarray:
-        """Rows (head, k-tile, first CSC entry, end CSC entry, partial slot or -1)."""
-        return self._arr(self.header.bwd_sched_off, 5 * self.header.bwd_sched_len, np.int32).reshape(-1, 5)
+        """Rows as fwd_schedule over (head, k-tile) and CSC entries."""
+        return self._arr(self.header.bwd_sched_off, SA_SCHED_FIELDS * self.header.bwd_sched_len,
+                         np.int32).reshape(-1, SA_SCHED_FIELDS)
 
     def xcd_lists(self, which: str) -> np.ndarray:
         """[SA_XCDS, len] schedule indices per XCD ("fwd" or "bwd"), -1 = padding."""
@@ -298,8 +302,9 @@ def sparse_attn_fwd(layout: Layout, q, k, v, scale: float | None = None, out=Non
                     workspace=None, phases: int = SA_FWD_ALL):
     """Forward on the current torch stream: returns (o, lse).
 
-    ``phases`` selects which of the two launches run (``sparse_attn_fwd_phases``
-    in the C header); the default runs both.
+    ``workspace``: a uint8 device tensor of at least ``fwd_workspace_bytes``
+    bytes (allocated when omitted).  ``phases`` selects which of the two
+    launches run (``sparse_attn_fwd_phases`` in the C header).
     """
     import torch
     lib = load_library()
@@ -337,6 +342,8 @@ def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = N
 
     ``phases`` selects which of the three launches run (see
     ``sparse_attn_bwd_phases`` in the C header); the default runs all.
+    ``workspace``: a uint8 device tensor of at least ``bwd_workspace_bytes``
+    bytes (allocated when omitted).
     """
     import torch
     lib = load_library()

@@ -7,29 +7,26 @@
 //     dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale sum_j dS_ij k_j,
 //     dK_j = scale sum_i dS_ij q_i.
 //
-// Three launches on the caller's stream, none with atomics (deterministic):
-//   bwd_dq    one workgroup per query tile (the forward's tiling): D_i for its
-//             rows (kept in the workspace for the next pass), then a walk of
-//             the tile's CSR key tiles: S^T = K Q^T and dP^T = V dO^T on the
-//             MFMA units, P and dS in registers, dQ^T += K^T dS^T on the MFMA
-//             units; dQ written once;
+// Launches on the caller's stream:
+//   bwd_dq    one workgroup per query tile (the forward's tiling, long tiles
+//             in chunks): D_i for its rows (kept in the workspace for the
+//             next pass), then a walk of the tile's CSR key tiles: S^T = K Q^T
+//             and dP^T = V dO^T on the MFMA units, P and dS in registers,
+//             dQ^T += K^T dS^T on the MFMA units; dQ written once;
 //   bwd_dkdv  one workgroup per key tile (or per chunk of a long key tile's
 //             CSC list): each wave owns 32 keys with K, V held as MFMA
 //             operands and dK, dV accumulated in registers; per query tile,
 //             Q, dO (row-major), LSE and D are staged in LDS; S = Q K^T and
 //             dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T
-//             through transposing LDS reads).  Unsplit
-//             tiles write dK, dV (exact zeros for keys no query reads); chunks
-//             of split tiles write float32 partial sums to the workspace;
-//   bwd_reduce sums the chunks of each split key tile (dK, dV) and of each
-//             split query tile (dQ) in chunk order.
-// Long query tiles are split into chunks for the dQ pass exactly as for the
-// forward (float32 partial dQ per chunk).
+//             through transposing LDS reads).  Unsplit tiles write dK, dV
+//             (exact zeros for keys no query reads).
+// Chunks of split tiles store float32 partial sums in the workspace; a third
+// launch (bwd_merge) sums the chunks of every split key tile (dK, dV) and
+// split query tile (dQ) in chunk order and writes their gradients.  No
+// atomics: every result is deterministic.
 
 #include <limits.h>
 #include <math.h>
-
-#include <type_traits>
 
 #include "device_common.hpp"
 
@@ -39,14 +36,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
   const uint8_t* blob;
-  const int32_t* qsched;    // (head, q-tile, e0, e1, slot): the forward schedule
-  const int32_t* ksched;    // (head, k-tile, e0, e1, slot)
-  const int32_t* rsched;    // (head, k-tile, slot0, chunks)
-  const int32_t* csched;    // (head, q-tile, slot0, chunks)
+  const int32_t* qsched;    // query-tile entries (the forward schedule), SA_SCHED_FIELDS ints
+  const int32_t* ksched;    // key-tile entries, SA_SCHED_FIELDS ints
   const int32_t* qxl;       // per-XCD lists over qsched
   const int32_t* kxl;       // per-XCD lists over ksched
   int32_t qxl_len, kxl_len;
-  int32_t B, H, n, num_slots, num_qslots, red_len;
+  int32_t B, H, n, num_slots, num_qslots;
+  const int32_t* rsched;    // (head, k-tile, first slot, chunks) of each split key tile
+  const int32_t* csched;    // (head, q-tile, first slot, chunks) of each split query tile
+  int32_t kgroups;          // split key tiles (rsched entries)
   const bf16* q;
   const bf16* k;
   const bf16* v;
@@ -81,8 +79,8 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.qxl, p.qxl_len, p.B, &b, &item)) return;
-  const int32_t* it5 = p.qsched + 5 * item;
-  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
+  const int32_t* it8 = p.qsched + SA_SCHED_FIELDS * item;
+  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3], slot = it8[4];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
@@ -260,8 +258,9 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   __shared__ __attribute__((aligned(16))) bf16 sq[2][QS * RS];
   __shared__ __attribute__((aligned(16))) bf16 sdo[2][QS * RS];
-  __shared__ __attribute__((aligned(16))) float slse[2][QS];
-  __shared__ __attribute__((aligned(16))) float sdd[2][QS];
+  // (LSE * log2(e), D) of each staged query row, interleaved so that the
+  // values of 8 consecutive rows are four 16-byte reads.
+  __shared__ __attribute__((aligned(16))) float smeta[2][2 * QS];
   __shared__ __attribute__((aligned(16))) int32_t slo[2][QS];
   __shared__ __attribute__((aligned(16))) int32_t shi[2][QS];
 
@@ -269,8 +268,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.kxl, p.kxl_len, p.B, &b, &item)) return;
-  const int32_t* it5 = p.ksched + 5 * item;
-  const int head = it5[0], kt = it5[1], c0 = it5[2], c1 = it5[3], slot = it5[4];
+  const int32_t* it8 = p.ksched + SA_SCHED_FIELDS * item;
+  const int head = it8[0], kt = it8[1], c0 = it8[2], c1 = it8[3], slot = it8[4];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
@@ -327,10 +326,11 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     if (tid < QS) {
       const int r = r0 + tid;
       const int tk = rtok;
-      // FULL tiles stage open bounds so that one branch-free mask serves both.
-      const bool full_tile = pv.bflag[e] == SA_TILE_FULL;
-      lo_r = full_tile ? INT_MIN : pv.lo[r];
-      hi_r = full_tile ? INT_MAX : pv.hi[r];
+      // Row intervals are read only by the masked body (PARTIAL tiles).
+      if (pv.bflag[e] != SA_TILE_FULL) {
+        lo_r = pv.lo[r];
+        hi_r = pv.hi[r];
+      }
       lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : 0.f;
       dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
     }
@@ -343,8 +343,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       *reinterpret_cast<u32x4*>(&sdo[buf][j * RS + cc * 8]) = doreg[i];
     }
     if (tid < QS) {
-      slse[buf][tid] = lse_r;
-      sdd[buf][tid] = dd_r;
+      *reinterpret_cast<floatx2*>(&smeta[buf][2 * tid]) = floatx2{lse_r, dd_r};
       slo[buf][tid] = lo_r;
       shi[buf][tid] = hi_r;
     }
@@ -364,6 +363,9 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       if (step + 2 < nsteps) iload(step + 2);
     }
 
+    // PARTIAL tiles set hidden scores to -inf (probability 0) under one
+    // uniform branch; FULL tiles (every pair visible) skip it.
+    const bool full = pv.bflag[c0 + step / NSTEP] == SA_TILE_FULL;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       floatx16 s = floatx16{}, dp = floatx16{};
@@ -374,27 +376,37 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
         dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[buf][roff + 16 * c]), vq[c], dp);
       }
       // Register r of half g: query 32*qb + kappa(r, g); lane = key.
+      if (!full) {
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const int qloc = 32 * qb + 16 * h8 + 8 * g;
+          const int4 loa = *reinterpret_cast<const int4*>(&slo[buf][qloc]);
+          const int4 lob = *reinterpret_cast<const int4*>(&slo[buf][qloc + 4]);
+          const int4 hia = *reinterpret_cast<const int4*>(&shi[buf][qloc]);
+          const int4 hib = *reinterpret_cast<const int4*>(&shi[buf][qloc + 4]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int qlo = j < 4 ? loa[j] : lob[j - 4];
+            const int qhi = j < 4 ? hia[j] : hib[j - 4];
+            const int r = 8 * h8 + j;
+            s[r] = (kpos >= qlo && kpos <= qhi) ? s[r] : -INFINITY;
+          }
+        }
+      }
       float pr[16], ds[16];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const int qloc = 32 * qb + 16 * h8 + 8 * g;
-        const floatx4 la = *reinterpret_cast<const floatx4*>(&slse[buf][qloc]);
-        const floatx4 lb = *reinterpret_cast<const floatx4*>(&slse[buf][qloc + 4]);
-        const floatx4 da = *reinterpret_cast<const floatx4*>(&sdd[buf][qloc]);
-        const floatx4 db = *reinterpret_cast<const floatx4*>(&sdd[buf][qloc + 4]);
-        const int4 loa = *reinterpret_cast<const int4*>(&slo[buf][qloc]);
-        const int4 lob = *reinterpret_cast<const int4*>(&slo[buf][qloc + 4]);
-        const int4 hia = *reinterpret_cast<const int4*>(&shi[buf][qloc]);
-        const int4 hib = *reinterpret_cast<const int4*>(&shi[buf][qloc + 4]);
+        const floatx4* mp = reinterpret_cast<const floatx4*>(&smeta[buf][2 * qloc]);
+        const floatx4 m0 = mp[0], m1 = mp[1], m2 = mp[2], m3 = mp[3];
+        const float mv[16] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3],
+                              m2[0], m2[1], m2[2], m2[3], m3[0], m3[1], m3[2], m3[3]};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * h8 + j;
-          const float l2 = j < 4 ? la[j] : lb[j - 4];
-          const float dd = j < 4 ? da[j] : db[j - 4];
-          const int qlo = j < 4 ? loa[j] : lob[j - 4];
-          const int qhi = j < 4 ? hia[j] : hib[j - 4];
-          float pp = fast_exp2(fmaf(s[r], c2, -l2));
-          pp = (kpos >= qlo && kpos <= qhi) ? pp : 0.f;
+          const float l2 = mv[2 * j];
+          const float dd = mv[2 * j + 1];
+          const float pp = fast_exp2(fmaf(s[r], c2, -l2));
           pr[r] = pp;
           ds[r] = pp * (dp[r] - dd);
         }
@@ -463,54 +475,46 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 // --------------------------------------------------------------------------
 // Sum the chunk partials of each split key tile (chunk order) -> dK, dV.
 // --------------------------------------------------------------------------
+// Merge launch: the chunks of each split key tile (dK, dV: 2 * BK * 64
+// floats per slot) and of each split query tile (dQ: BQ * 64 floats per slot)
+// are summed in chunk order.  One workgroup of 256 threads per (batch
+// element, group, 2048-float block); thread = 8 consecutive floats.
 template <int BQ, int BK>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_merge_kernel(BwdParams p) {
+  constexpr int KPER = 2 * BK * kD, QPER = BQ * kD;  // floats per slot
+  constexpr int KBLK = KPER / 2048, QBLK = QPER / 2048;
   const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
-  if (item >= p.red_len) {
-    // dQ chunks of a split query tile
-    const int32_t* c4 = p.csched + 4 * (item - p.red_len);
-    const int head = c4[0], qt = c4[1], slot0 = c4[2], chunks = c4[3];
-    const PatView pv = pattern_of_head(p.blob, head);
-    const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
-    constexpr int PERQ = BQ * kD;
-    const float* part0 = p.part_dq + (size_t(b) * p.num_qslots + slot0) * PERQ;
-    for (int idx = threadIdx.x * 8; idx < PERQ; idx += 256 * 8) {
-      floatx4 a = floatx4{}, c = floatx4{};
-      for (int ch = 0; ch < chunks; ++ch) {
-        const floatx4* src = reinterpret_cast<const floatx4*>(part0 + size_t(ch) * PERQ + idx);
-        a += src[0];
-        c += src[1];
-      }
-      const int tok = pv.qmap[qt * BQ + idx / kD];
-      if (tok < 0) continue;
-      float tmp[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-      *reinterpret_cast<bf16x8*>(p.dq + (base + tok) * kD + idx % kD) = pack_bf16x8(tmp);
-    }
-    return;
-  }
-  const int32_t* it4 = p.rsched + 4 * item;
-  const int head = it4[0], kt = it4[1], slot0 = it4[2], chunks = it4[3];
+  int gi = blockIdx.x / p.B;
+  const bool key_tile = gi < p.kgroups * KBLK;
+  if (!key_tile) gi -= p.kgroups * KBLK;
+  const int blk = key_tile ? gi % KBLK : gi % QBLK;
+  const int32_t* g4 = key_tile ? p.rsched + 4 * (gi / KBLK) : p.csched + 4 * (gi / QBLK);
+  const int head = g4[0], tile = g4[1], slot0 = g4[2], chunks = g4[3];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
-  constexpr int PER = 2 * BK * kD;  // floats per slot
-  const float* part0 = p.partial + (size_t(b) * p.num_slots + slot0) * PER;
-  for (int idx = threadIdx.x * 8; idx < PER; idx += 256 * 8) {
-    floatx4 a = floatx4{}, c = floatx4{};
-    for (int ch = 0; ch < chunks; ++ch) {
-      const floatx4* src = reinterpret_cast<const floatx4*>(part0 + size_t(ch) * PER + idx);
-      a += src[0];
-      c += src[1];
-    }
+  const int idx = blk * 2048 + threadIdx.x * 8;
+  const int per = key_tile ? KPER : QPER;
+  const float* part0 = key_tile ? p.partial + (size_t(b) * p.num_slots + slot0) * KPER
+                                : p.part_dq + (size_t(b) * p.num_qslots + slot0) * QPER;
+  bf16* dst;
+  if (key_tile) {
     const int t = idx / (BK * kD);  // 0: dK, 1: dV
-    const int key = (idx / kD) % BK;
-    const int f = idx % kD;
-    const int tok = pv.kmap[kt * BK + key];
-    if (tok < 0) continue;
-    float tmp[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-    bf16* dst = (t == 0 ? p.dk : p.dv) + (base + tok) * kD + f;
-    *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
+    const int tok = pv.kmap[tile * BK + (idx / kD) % BK];
+    if (tok < 0) return;
+    dst = (t == 0 ? p.dk : p.dv) + (base + tok) * kD + idx % kD;
+  } else {
+    const int tok = pv.qmap[tile * BQ + idx / kD];
+    if (tok < 0) return;
+    dst = p.dq + (base + tok) * kD + idx % kD;
   }
+  floatx4 a = floatx4{}, c = floatx4{};
+  for (int ch = 0; ch < chunks; ++ch) {
+    const floatx4* src = reinterpret_cast<const floatx4*>(part0 + size_t(ch) * per + idx);
+    a += src[0];
+    c += src[1];
+  }
+  float tmp[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
 }
 
 }  // namespace sa
@@ -524,14 +528,22 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t kv_partial_bytes(int B, int32_t num_slots, int32_t bk) {
-  return round256(size_t(B) * size_t(num_slots) * 2 * size_t(bk) * sa::kD * sizeof(float));
-}
+// Workspace: [D float32[B, H, n]] [dK, dV partials float32[B, slots, 2, BK,
+// 64]] [dQ partials float32[B, query slots, BQ, 64]]; each part starts on a
+// 256-byte boundary.
+struct BwdWorkspace {
+  size_t dsum, partial, part_dq, total;
+};
 
-size_t workspace_bytes(int64_t rows, int B, int32_t num_slots, int32_t bk, int32_t num_qslots,
-                       int32_t bq) {
-  return round256(size_t(rows) * sizeof(float)) + kv_partial_bytes(B, num_slots, bk) +
-         size_t(B) * size_t(num_qslots) * size_t(bq) * sa::kD * sizeof(float);
+BwdWorkspace bwd_workspace_layout(int B, int H, const sa_blob_header& h) {
+  BwdWorkspace w{};
+  w.dsum = 0;
+  w.partial = w.dsum + round256(size_t(B) * size_t(H) * size_t(h.n) * sizeof(float));
+  w.part_dq = w.partial + round256(size_t(B) * size_t(h.num_slots) * 2 * size_t(h.block_k) *
+                                   sa::kD * sizeof(float));
+  w.total = w.part_dq + round256(size_t(B) * size_t(h.num_qslots) * size_t(h.block_q) * sa::kD *
+                                 sizeof(float));
+  return w;
 }
 
 }  // namespace
@@ -546,8 +558,7 @@ extern "C" int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, in
   if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
   if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
   if (d != 64 || dtype != SA_BF16) return SA_EUNSUPPORTED;
-  *bytes = workspace_bytes(int64_t(B) * H * h.n, B, h.num_slots, h.block_k, h.num_qslots,
-                           h.block_q);
+  *bytes = bwd_workspace_layout(B, H, h).total;
   return SA_OK;
 }
 
@@ -570,26 +581,27 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   if (rc != SA_OK) return rc;
   sa_blob_header h;
   memcpy(&h, blob_host, sizeof(h));
-  const int64_t rows = int64_t(B) * H * li.n;
   if (B == 0) return SA_OK;  // empty batch: pointers may be NULL
-  if (ws_bytes < workspace_bytes(rows, B, h.num_slots, bk, h.num_qslots, bq)) return SA_ESIZE;
+  const BwdWorkspace wl = bwd_workspace_layout(B, H, h);
+  if (ws_bytes < wl.total) return SA_ESIZE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return SA_EINVAL;
   const int64_t gq = int64_t(SA_XCDS) * li.fwd_xl_len * B;
   const int64_t gk = int64_t(SA_XCDS) * li.bwd_xl_len * B;
-  const int64_t gr = int64_t(h.red_sched_len + h.comb_sched_len) * B;
-  if (gq > INT32_MAX || gk > INT32_MAX || gr > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t gm = (int64_t(h.red_sched_len) * (2 * bk * kD / 2048) +
+                      int64_t(h.comb_sched_len) * (bq * kD / 2048)) * B;
+  if (gq > INT32_MAX || gk > INT32_MAX || gm > INT32_MAX) return SA_EUNSUPPORTED;
 
   BwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
   prm.qsched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
   prm.ksched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
+  prm.num_qslots = h.num_qslots;
+  prm.kgroups = h.red_sched_len;
   prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
   prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
-  prm.num_qslots = h.num_qslots;
-  prm.red_len = h.red_sched_len;
   prm.qxl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
   prm.kxl = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xl_off);
   prm.qxl_len = li.fwd_xl_len;
@@ -607,12 +619,10 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.dq = static_cast<bf16*>(dq);
   prm.dk = static_cast<bf16*>(dk);
   prm.dv = static_cast<bf16*>(dv);
-  prm.dsum = static_cast<float*>(workspace);
-  prm.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                         round256(size_t(rows) * sizeof(float)));
-  prm.part_dq = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                         round256(size_t(rows) * sizeof(float)) +
-                                         kv_partial_bytes(B, h.num_slots, bk));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  prm.dsum = reinterpret_cast<float*>(ws + wl.dsum);
+  prm.partial = reinterpret_cast<float*>(ws + wl.partial);
+  prm.part_dq = reinterpret_cast<float*>(ws + wl.part_dq);
   prm.scale = sc;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -636,13 +646,13 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_dkdv_kernel<64, 64>), gk, 128);
     else SA_LAUNCH((bwd_dkdv_kernel<128, 64>), gk, 128);
   }
-  if ((phases & SA_BWD_REDUCE) && gr > 0) {
-    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<32, 32>), gr, 256);
-    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_reduce_kernel<32, 64>), gr, 256);
-    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<64, 32>), gr, 256);
-    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_reduce_kernel<64, 64>), gr, 256);
-    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_reduce_kernel<128, 32>), gr, 256);
-    else SA_LAUNCH((bwd_reduce_kernel<128, 64>), gr, 256);
+  if ((phases & SA_BWD_MERGE) && gm > 0) {
+    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_merge_kernel<32, 32>), gm, 256);
+    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_merge_kernel<32, 64>), gm, 256);
+    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_merge_kernel<64, 32>), gm, 256);
+    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_merge_kernel<64, 64>), gm, 256);
+    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_merge_kernel<128, 32>), gm, 256);
+    else SA_LAUNCH((bwd_merge_kernel<128, 64>), gm, 256);
   }
 #undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;

@@ -21,6 +21,11 @@
 // log-sum-exp that the backward pass rebuilds probabilities from (report
 // section 3.4).  A wave skips the arithmetic of a tile none of its rows can
 // see (it still takes part in the staging).
+//
+// Query tiles with long CSR lists run as several chunks (one workgroup each).
+// A chunk stores its unnormalised O, running max and running sum in float32;
+// a second launch merges the chunks of each split tile exactly (rescaling
+// each to the common max) in chunk order.
 
 #include <math.h>
 
@@ -35,9 +40,8 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
 
 struct FwdParams {
   const uint8_t* blob;
-  const int32_t* sched;   // (head, q-tile, e0, e1, slot)
+  const int32_t* sched;   // SA_SCHED_FIELDS ints per query-tile entry
   const int32_t* xl;      // per-XCD lists of schedule entries
-  const int32_t* csched;  // (head, q-tile, slot0, chunks) of split query tiles
   int32_t xl_len;
   int32_t B, H, n, num_qslots;
   const void* q;
@@ -48,12 +52,51 @@ struct FwdParams {
   float* part_o;  // [B, num_qslots, BQ, 64]: unnormalised O of a chunk
   float* part_m;  // [B, num_qslots, BQ]: running max (base 2)
   float* part_l;  // [B, num_qslots, BQ]: running sum
+  const int32_t* csched;  // (head, q-tile, first slot, chunks) of each split query tile
   float scale_log2;  // softmax scale * log2(e)
 };
 
+// Merge of a split query tile (all chunks have stored their partials): per
+// row, m = max of the chunk maxima, O = sum_c 2^(m_c - m) acc_c / l with
+// l = sum_c 2^(m_c - m) l_c, LSE = (m + log2 l) ln 2.  Chunks are taken in
+// order.  One thread per (row, 8 features).
+template <typename T, int BQ>
+__device__ __forceinline__ void fwd_merge_row(const FwdParams& p, const PatView& pv, size_t base,
+                                              int b, int qt, int slot0, int chunks, int row,
+                                              int part) {
+  {
+    const int tok = pv.qmap[qt * BQ + row];
+    if (tok < 0) return;
+    const size_t r0 = (size_t(b) * p.num_qslots + slot0) * BQ + row;
+    float m = -INFINITY;
+    for (int c = 0; c < chunks; ++c) m = fmaxf(m, p.part_m[r0 + size_t(c) * BQ]);
+    float l = 0.f;
+    floatx4 a = floatx4{}, a2 = floatx4{};
+    for (int c = 0; c < chunks; ++c) {
+      const size_t rc = r0 + size_t(c) * BQ;
+      const float wgt = fast_exp2(p.part_m[rc] - m);
+      l += wgt * p.part_l[rc];
+      const floatx4* src = reinterpret_cast<const floatx4*>(p.part_o + rc * kD + 8 * part);
+      a += wgt * src[0];
+      a2 += wgt * src[1];
+    }
+    const float inv = 1.0f / l;
+    float tmp[8] = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv,
+                    a2[0] * inv, a2[1] * inv, a2[2] * inv, a2[3] * inv};
+    T* dst = static_cast<T*>(p.o) + (base + size_t(tok)) * kD + 8 * part;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
+    } else {
+      *reinterpret_cast<floatx4*>(dst) = floatx4{tmp[0], tmp[1], tmp[2], tmp[3]};
+      *reinterpret_cast<floatx4*>(dst + 4) = floatx4{tmp[4], tmp[5], tmp[6], tmp[7]};
+    }
+    if (part == 0) p.lse[base + tok] = (m + log2f(l)) * kLn2;
+  }
+}
+
 // Epilogue shared by both element types.  Register r of half g of oacc[fb]
 // holds feature 32*fb + kappa(r, g) of the lane's query row.  Unsplit tiles
-// write O = acc / l and LSE; chunks of split tiles write (acc, m, l).
+// write O = acc / l and LSE; chunks of split tiles store (acc, m, l).
 template <typename T, int BQ>
 __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 (&oacc)[2],
                                              float m_run, float l_run, int tok, size_t base,
@@ -117,8 +160,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int32_t* it5 = p.sched + 5 * item;
-  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
+  const int32_t* it8 = p.sched + SA_SCHED_FIELDS * item;
+  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const bf16* qg = static_cast<const bf16*>(p.q) + base * kD;
@@ -259,7 +302,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  fwd_epilogue<bf16, BQ>(p, oacc, m_run, l_run, tok, base, b, slot, w * 32 + l32, g);
+  fwd_epilogue<bf16, BQ>(p, oacc, m_run, l_run, tok, base, b, it8[4], w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------
@@ -281,8 +324,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
   const int g = lane >> 5, l32 = lane & 31;
   int b, item;
   if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int32_t* it5 = p.sched + 5 * item;
-  const int head = it5[0], qt = it5[1], e0 = it5[2], e1 = it5[3], slot = it5[4];
+  const int32_t* it8 = p.sched + SA_SCHED_FIELDS * item;
+  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
   const PatView pv = pattern_of_head(p.blob, head);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const float* qg = static_cast<const float*>(p.q) + base * kD;
@@ -392,7 +435,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  fwd_epilogue<float, BQ>(p, oacc, m_run, l_run, tok, base, b, slot, w * 32 + l32, g);
+  fwd_epilogue<float, BQ>(p, oacc, m_run, l_run, tok, base, b, it8[4], w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------
@@ -401,43 +444,18 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 // l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, LSE = (m + log2 l) ln 2.
 // Chunks are summed in chunk order.  8 threads per row (8 features each).
 // --------------------------------------------------------------------------
+// Merge launch: one workgroup of 256 threads per (batch element, split query
+// tile, 32-row block of the tile); thread = (row, 8 features).
 template <typename T, int BQ>
-__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  constexpr int RB = BQ / 32;  // row blocks per tile
   const int b = blockIdx.x % p.B;
-  const int item = blockIdx.x / p.B;
-  const int32_t* it4 = p.csched + 4 * item;
-  const int head = it4[0], qt = it4[1], slot0 = it4[2], chunks = it4[3];
-  const PatView pv = pattern_of_head(p.blob, head);
-  const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
-  for (int t = threadIdx.x; t < BQ * 8; t += 256) {
-    const int row = t >> 3, part = t & 7;
-    const int tok = pv.qmap[qt * BQ + row];
-    if (tok < 0) continue;
-    const size_t r0 = (size_t(b) * p.num_qslots + slot0) * BQ + row;
-    float m = -INFINITY;
-    for (int c = 0; c < chunks; ++c) m = fmaxf(m, p.part_m[r0 + size_t(c) * BQ]);
-    float l = 0.f;
-    floatx4 a = floatx4{}, a2 = floatx4{};
-    for (int c = 0; c < chunks; ++c) {
-      const size_t rc = r0 + size_t(c) * BQ;
-      const float wgt = fast_exp2(p.part_m[rc] - m);
-      l += wgt * p.part_l[rc];
-      const floatx4* src = reinterpret_cast<const floatx4*>(p.part_o + rc * kD + 8 * part);
-      a += wgt * src[0];
-      a2 += wgt * src[1];
-    }
-    const float inv = 1.0f / l;
-    float tmp[8] = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv,
-                    a2[0] * inv, a2[1] * inv, a2[2] * inv, a2[3] * inv};
-    T* dst = static_cast<T*>(p.o) + (base + size_t(tok)) * kD + 8 * part;
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<bf16x8*>(dst) = pack_bf16x8(tmp);
-    } else {
-      *reinterpret_cast<floatx4*>(dst) = floatx4{tmp[0], tmp[1], tmp[2], tmp[3]};
-      *reinterpret_cast<floatx4*>(dst + 4) = floatx4{tmp[4], tmp[5], tmp[6], tmp[7]};
-    }
-    if (part == 0) p.lse[base + tok] = (m + log2f(l)) * kLn2;
-  }
+  const int gi = blockIdx.x / p.B;
+  const int32_t* c4 = p.csched + 4 * (gi / RB);
+  const PatView pv = pattern_of_head(p.blob, c4[0]);
+  const size_t base = (size_t(b) * p.H + c4[0]) * size_t(p.n);
+  const int row = (gi % RB) * 32 + (threadIdx.x >> 3);
+  fwd_merge_row<T, BQ>(p, pv, base, b, c4[1], c4[2], c4[3], row, threadIdx.x & 7);
 }
 
 }  // namespace sa
@@ -449,11 +467,24 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p) {
 
 namespace {
 
-size_t fwd_workspace_bytes(int B, int32_t num_qslots, int32_t bq) {
-  const size_t rows = size_t(B) * size_t(num_qslots) * size_t(bq);
-  const size_t o = (rows * sa::kD * sizeof(float) + 255) & ~size_t(255);
-  const size_t ml = (rows * sizeof(float) + 255) & ~size_t(255);
-  return o + 2 * ml;
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: [partial O float32[B, slots, BQ, 64]] [partial max float32[B,
+// slots, BQ]] [partial sum, same]; each part starts on a 256-byte boundary.
+// Empty when no query tile is split.
+struct FwdWorkspace {
+  size_t part_o, part_m, part_l, total;
+};
+
+FwdWorkspace fwd_workspace_layout(int B, const sa_blob_header& h) {
+  FwdWorkspace w{};
+  if (h.num_qslots == 0 || B == 0) return w;
+  const size_t rows = size_t(B) * size_t(h.num_qslots) * size_t(h.block_q);
+  w.part_o = 0;
+  w.part_m = w.part_o + round256(rows * sa::kD * sizeof(float));
+  w.part_l = w.part_m + round256(rows * sizeof(float));
+  w.total = w.part_l + round256(rows * sizeof(float));
+  return w;
 }
 
 }  // namespace
@@ -468,7 +499,7 @@ extern "C" int sparse_attn_fwd_workspace(const void* blob_host, int B, int H, in
   if (B < 0 || H < 1 || H != h.num_heads) return SA_EINVAL;
   if (dtype != SA_BF16 && dtype != SA_FP32) return SA_EINVAL;
   if (d != 64) return SA_EUNSUPPORTED;
-  *bytes = fwd_workspace_bytes(B, h.num_qslots, h.block_q);
+  *bytes = fwd_workspace_layout(B, h).total;
   return SA_OK;
 }
 
@@ -491,39 +522,35 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
   const bool shape_ok = dtype == SA_BF16 ? (bk == 32 || bk == 64) : (bk == 32);
   if (!shape_ok) return SA_EUNSUPPORTED;
   if (B == 0 || li.fwd_xl_len == 0) return SA_OK;  // empty batch: pointers may be NULL
-  const size_t need = fwd_workspace_bytes(B, h.num_qslots, bq);
-  if (ws_bytes < need) return SA_ESIZE;
+  const FwdWorkspace wl = fwd_workspace_layout(B, h);
+  if (ws_bytes < wl.total) return SA_ESIZE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      (need > 0 && !aligned16(workspace)))
+      (wl.total > 0 && !aligned16(workspace)))
     return SA_EINVAL;
   const int64_t grid = int64_t(SA_XCDS) * li.fwd_xl_len * B;
-  const int64_t cgrid = int64_t(h.comb_sched_len) * B;
-  if (grid > INT32_MAX || cgrid > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t mgrid = int64_t(h.comb_sched_len) * (bq / 32) * B;
+  if (grid > INT32_MAX || mgrid > INT32_MAX) return SA_EUNSUPPORTED;
 
   FwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
   prm.sched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
   prm.xl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
-  prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
   prm.xl_len = li.fwd_xl_len;
   prm.B = B;
   prm.H = H;
   prm.n = int32_t(li.n);
   prm.num_qslots = h.num_qslots;
+  prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
   prm.q = q;
   prm.k = k;
   prm.v = v;
   prm.o = o;
   prm.lse = lse;
-  {
-    const size_t rows = size_t(B) * size_t(h.num_qslots) * size_t(bq);
-    const size_t ob = (rows * kD * sizeof(float) + 255) & ~size_t(255);
-    const size_t mb = (rows * sizeof(float) + 255) & ~size_t(255);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    prm.part_o = need ? reinterpret_cast<float*>(ws) : nullptr;
-    prm.part_m = need ? reinterpret_cast<float*>(ws + ob) : nullptr;
-    prm.part_l = need ? reinterpret_cast<float*>(ws + ob + mb) : nullptr;
-  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool split = wl.total > 0;
+  prm.part_o = split ? reinterpret_cast<float*>(ws + wl.part_o) : nullptr;
+  prm.part_m = split ? reinterpret_cast<float*>(ws + wl.part_m) : nullptr;
+  prm.part_l = split ? reinterpret_cast<float*>(ws + wl.part_l) : nullptr;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -543,15 +570,15 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
       else SA_LAUNCH((fwd_f32_kernel<128, 32>), grid, 256);
     }
   }
-  if ((phases & SA_FWD_COMBINE) && cgrid > 0) {
+  if ((phases & SA_FWD_MERGE) && mgrid > 0) {
     if (dtype == SA_BF16) {
-      if (bq == 32) SA_LAUNCH((fwd_combine_kernel<bf16, 32>), cgrid, 256);
-      else if (bq == 64) SA_LAUNCH((fwd_combine_kernel<bf16, 64>), cgrid, 256);
-      else SA_LAUNCH((fwd_combine_kernel<bf16, 128>), cgrid, 256);
+      if (bq == 32) SA_LAUNCH((fwd_merge_kernel<bf16, 32>), mgrid, 256);
+      else if (bq == 64) SA_LAUNCH((fwd_merge_kernel<bf16, 64>), mgrid, 256);
+      else SA_LAUNCH((fwd_merge_kernel<bf16, 128>), mgrid, 256);
     } else {
-      if (bq == 32) SA_LAUNCH((fwd_combine_kernel<float, 32>), cgrid, 256);
-      else if (bq == 64) SA_LAUNCH((fwd_combine_kernel<float, 64>), cgrid, 256);
-      else SA_LAUNCH((fwd_combine_kernel<float, 128>), cgrid, 256);
+      if (bq == 32) SA_LAUNCH((fwd_merge_kernel<float, 32>), mgrid, 256);
+      else if (bq == 64) SA_LAUNCH((fwd_merge_kernel<float, 64>), mgrid, 256);
+      else SA_LAUNCH((fwd_merge_kernel<float, 128>), mgrid, 256);
     }
   }
 #undef SA_LAUNCH

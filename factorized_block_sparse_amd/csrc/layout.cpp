@@ -223,6 +223,7 @@ struct Writer {
 struct SchedItem {
   int32_t head, tile, work;
   int32_t e0 = 0, e1 = 0, slot = -1;
+  int32_t group = -1, slot0 = -1, nchunks = 1;  // split tile: merge group, its slots
 };
 
 // Per-XCD lists over the sorted schedule `sorted` (work in sorted order):
@@ -264,22 +265,15 @@ int32_t xcd_lists(const std::vector<SchedItem>& sorted, std::vector<int32_t>& ou
   return len;
 }
 
-// Heaviest first; ties keep (head, tile) order.  `fields` = 2 (head, tile) or
-// 5 (head, tile, e0, e1, slot).
-std::vector<int32_t> sorted_schedule(std::vector<SchedItem>& items, int fields) {
+// Heaviest first; ties keep (head, tile) order.  SA_SCHED_FIELDS ints per
+// entry: (head, tile, e0, e1, slot, group, slot0, nchunks).
+std::vector<int32_t> sorted_schedule(std::vector<SchedItem>& items) {
   std::stable_sort(items.begin(), items.end(),
                    [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
   std::vector<int32_t> out;
-  out.reserve(items.size() * fields);
-  for (const auto& it : items) {
-    out.push_back(it.head);
-    out.push_back(it.tile);
-    if (fields == 5) {
-      out.push_back(it.e0);
-      out.push_back(it.e1);
-      out.push_back(it.slot);
-    }
-  }
+  out.reserve(items.size() * SA_SCHED_FIELDS);
+  for (const auto& it : items)
+    out.insert(out.end(), {it.head, it.tile, it.e0, it.e1, it.slot, it.group, it.slot0, it.nchunks});
   return out;
 }
 
@@ -342,6 +336,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         continue;
       }
       const int32_t chunks = (len + qcap - 1) / qcap;
+      const int32_t group = int32_t(comb_sched.size() / 4);
       comb_sched.insert(comb_sched.end(), {h, qt, num_qslots, chunks});
       for (int32_t c = 0; c < chunks; ++c) {
         SchedItem it{h, qt, 0};
@@ -349,6 +344,9 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         it.e1 = r0 + int32_t(int64_t(len) * (c + 1) / chunks);
         it.work = it.e1 - it.e0;
         it.slot = num_qslots + c;
+        it.group = group;
+        it.slot0 = num_qslots;
+        it.nchunks = chunks;
         fwd_items.push_back(it);
       }
       num_qslots += chunks;
@@ -365,6 +363,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       }
       // Split into `chunks` nearly equal runs of CSC entries, one partial slot each.
       const int32_t chunks = (len + cap - 1) / cap;
+      const int32_t group = int32_t(red_sched.size() / 4);
       red_sched.insert(red_sched.end(), {h, kt, num_slots, chunks});
       for (int32_t c = 0; c < chunks; ++c) {
         SchedItem it{h, kt, 0};
@@ -372,13 +371,16 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         it.e1 = c0 + int32_t(int64_t(len) * (c + 1) / chunks);
         it.work = it.e1 - it.e0 + 1;
         it.slot = num_slots + c;
+        it.group = group;
+        it.slot0 = num_slots;
+        it.nchunks = chunks;
         bwd_items.push_back(it);
       }
       num_slots += chunks;
     }
   }
-  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items, 5);
-  const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items, 5);
+  const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
+  const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
   std::vector<int32_t> fwd_xl, bwd_xl;
   const int32_t fwd_xl_len = xcd_lists(fwd_items, fwd_xl);
   const int32_t bwd_xl_len = xcd_lists(bwd_items, bwd_xl);
@@ -497,9 +499,9 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
     return SA_EINVAL;
   if (!in_blob(h.head_pattern_off, 4 * int64_t(h.num_heads), total) ||
       !in_blob(h.pattern_off, int64_t(sizeof(sa_pattern_rec)) * h.num_patterns, total) ||
-      !in_blob(h.fwd_sched_off, 20 * int64_t(h.fwd_sched_len), total) ||
+      !in_blob(h.fwd_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.fwd_sched_len), total) ||
       !in_blob(h.comb_sched_off, 16 * int64_t(h.comb_sched_len), total) || h.num_qslots < 0 ||
-      !in_blob(h.bwd_sched_off, 20 * int64_t(h.bwd_sched_len), total) ||
+      !in_blob(h.bwd_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.bwd_sched_len), total) ||
       !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0 ||
       !in_blob(h.fwd_xl_off, 4 * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
       !in_blob(h.bwd_xl_off, 4 * int64_t(SA_XCDS) * h.bwd_xl_len, total))

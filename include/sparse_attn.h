@@ -112,7 +112,8 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 5u
+#define SA_BLOB_VERSION 6u
+#define SA_SCHED_FIELDS 8
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
  * many rows (rounded down to whole query tiles, at least one) for the dK/dV
@@ -121,7 +122,7 @@ typedef struct {
  * way for the forward and dQ passes; chunk results are merged in a fixed
  * order.  A cap of at least n disables splitting. */
 #define SA_SPLIT_ROWS 1536
-#define SA_SPLIT_KEYS 1024
+#define SA_SPLIT_KEYS 2048
 /* Number of accelerator complex dies (XCDs, each with its own L2) that
  * workgroups are dealt to round-robin on MI355X. */
 #define SA_XCDS 8
@@ -157,10 +158,13 @@ typedef struct {
   int64_t total_bytes;
   int64_t head_pattern_off; /* int32[num_heads]: pattern index of each head */
   int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
-  int64_t fwd_sched_off;    /* int32[5 * fwd_sched_len]: (head, q-tile, first CSR entry,
-                               end CSR entry, partial slot or -1), heaviest first */
-  int64_t bwd_sched_off;    /* int32[5 * bwd_sched_len]: (head, k-tile, first CSC entry,
-                               end CSC entry, partial slot or -1), heaviest first */
+  int64_t fwd_sched_off;    /* int32[SA_SCHED_FIELDS * fwd_sched_len]: (head, q-tile,
+                               first CSR entry, end CSR entry, partial slot, merge group,
+                               first slot of the group, chunks of the group), heaviest
+                               first; unsplit tiles have slot = group = slot0 = -1 and
+                               chunks = 1 */
+  int64_t bwd_sched_off;    /* int32[SA_SCHED_FIELDS * bwd_sched_len]: the same fields over
+                               k-tiles and CSC entries */
   int32_t fwd_sched_len, bwd_sched_len;
   int64_t red_sched_off;    /* int32[4 * red_sched_len]: (head, k-tile, first slot, chunks) */
   int32_t red_sched_len;
@@ -190,26 +194,37 @@ int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_byte
 /* Check a blob's header and internal offsets (host). */
 int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes);
 
+/* Split tiles and the workspace.  A query tile that reads more than
+ * split_keys keys (a key tile read by more than split_rows query rows) runs as
+ * several workgroups, each over one chunk of its CSR (CSC) list.  Each chunk
+ * writes float32 partial results to the workspace; a merge launch combines
+ * the chunks of every split tile in chunk order and writes the tile's
+ * outputs.  No atomics: repeated calls are bitwise identical.
+ *
+ * Workspace (both passes): at least the size the *_workspace call returns,
+ * 16-byte aligned, in device memory; its contents on entry do not matter.
+ * Calls that share a workspace must not overlap in time (issue them on one
+ * stream). */
+
 /* Bytes of device workspace sparse_attn_fwd needs for these sizes (0 when
  * the layout splits no query tile; the workspace may then be NULL). */
 int sparse_attn_fwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
                               size_t* bytes);
 
 /* Forward (report sections 3.5 and 3.4): o [B,H,n,d] in dtype, lse [B,H,n]
- * float32.  scale <= 0 selects 1/sqrt(d).  workspace: ws_bytes >= the size
- * returned by sparse_attn_fwd_workspace, 16-byte aligned, contents on entry
- * irrelevant (it holds the partial results of split query tiles).  B == 0 is
- * a valid no-op (the tensor pointers may then be NULL). */
+ * float32.  scale <= 0 selects 1/sqrt(d).  B == 0 is a valid no-op (the
+ * tensor pointers may then be NULL). */
 int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
                     const void* q, const void* k, const void* v, void* o, float* lse,
                     void* workspace, size_t ws_bytes, float scale, void* stream);
 
-/* The forward as two separately launchable phases (same arguments, one
- * stream, in order): SA_FWD_MAIN runs the block-sparse kernel (unsplit query
- * tiles write O and LSE, chunks of split tiles write partial results to the
- * workspace); SA_FWD_COMBINE merges the chunks of split tiles in chunk order
- * and writes their O and LSE.  sparse_attn_fwd runs SA_FWD_ALL. */
-enum { SA_FWD_MAIN = 1, SA_FWD_COMBINE = 2, SA_FWD_ALL = 3 };
+/* The forward's two launches, separately (same arguments, one stream, in
+ * order): SA_FWD_MAIN runs the block-sparse kernel (unsplit query tiles
+ * write O and LSE, chunks of split tiles write partial results to the
+ * workspace); SA_FWD_MERGE merges the chunks of split tiles (the running
+ * maxima rescaled to their common maximum) and writes their O and LSE.
+ * sparse_attn_fwd runs SA_FWD_ALL. */
+enum { SA_FWD_MAIN = 1, SA_FWD_MERGE = 2, SA_FWD_ALL = 3 };
 int sparse_attn_fwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
                            int dtype, const void* q, const void* k, const void* v, void* o,
                            float* lse, void* workspace, size_t ws_bytes, float scale,
@@ -222,27 +237,24 @@ int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, int d, int dt
 /* Backward by recomputation from LSE (report section 3.4): gradients of
  * sum(O * dO) with respect to q, k, v, written in dtype.  `o` and `lse` must
  * be the forward's outputs for the same inputs and scale.  Keys no query
- * reads in a head get exact zeros.  workspace: ws_bytes >= the size returned
- * by sparse_attn_bwd_workspace, 16-byte aligned; its contents on entry do not
- * matter.  Only SA_BF16. */
+ * reads in a head get exact zeros.  Only SA_BF16. */
 int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
                     const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     void* workspace, size_t ws_bytes, float scale, void* stream);
 
-/* The backward as three separately launchable phases, for callers that
- * interleave other work between them or time them one by one:
- *   SA_BWD_DQ      per query tile (long tiles in chunks): D_i = dO_i . O_i
- *                  (kept in the workspace) and dQ, written in dtype, or
- *                  float32 partial sums of split tiles (workspace);
- *   SA_BWD_DKDV    per key tile (long tiles in chunks): dK, dV written in
- *                  dtype, or float32 partial sums of split tiles (workspace);
- *   SA_BWD_REDUCE  sums the partials of split query and key tiles in a fixed
- *                  order and writes their dQ, dK, dV.
+/* The backward's three launches, separately, for callers that interleave
+ * other work between them or time them one by one:
+ *   SA_BWD_DQ     per query tile (long tiles in chunks): D_i = dO_i . O_i
+ *                 (kept in the workspace) and dQ, or float32 partial dQ of
+ *                 split tiles (workspace);
+ *   SA_BWD_DKDV   per key tile (long tiles in chunks): dK and dV, or float32
+ *                 partial sums of split tiles (workspace);
+ *   SA_BWD_MERGE  sums the partials of split query and key tiles in a fixed
+ *                 order and writes their dQ, dK, dV.
  * Phases must run in this order on one stream with the same arguments and
- * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL).
- * Every phase is deterministic (no atomics). */
-enum { SA_BWD_DQ = 1, SA_BWD_DKDV = 2, SA_BWD_REDUCE = 4, SA_BWD_ALL = 7 };
+ * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL). */
+enum { SA_BWD_DQ = 1, SA_BWD_DKDV = 2, SA_BWD_MERGE = 4, SA_BWD_ALL = 7 };
 int sparse_attn_bwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
                            int dtype, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dO, void* dq, void* dk, void* dv,

@@ -37,9 +37,10 @@ SMALL = [
                                     HeadPattern("summary", 8, 8, 0), HeadPattern("stride", 1)]),
     ("single_row", 1, 1, 64, 64, [HeadPattern("local", 4), HeadPattern("summary", 4, 2, 0)]),
     # rows reading more than 1024 keys: forward / dQ chunks, combine and reduce launches
-    ("split_k32", 2, 1500, 64, 32, [HeadPattern("local", 1400), HeadPattern("stride", 1)]),
+    ("split_k32", 2, 1500, 64, 32, [HeadPattern("local", 1400), HeadPattern("stride", 1)], 1024),
     ("split_q128_k64", 1, 2200, 128, 64, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
-                                          HeadPattern("sameblock", 2048)]),
+                                          HeadPattern("sameblock", 2048)], 1024),
+    ("split_default_caps", 1, 2600, 64, 64, [HeadPattern("local", 2500), HeadPattern("summary", 64, 16, 2)]),
 ]
 
 
@@ -62,9 +63,12 @@ def _check_dense(layout, heads, B, n, inp, backward=True, fp32=False):
     return out
 
 
-@pytest.mark.parametrize("name,B,n,bq,bk,heads", SMALL, ids=[c[0] for c in SMALL])
-def test_small_cases_every_element(name, B, n, bq, bk, heads):
-    lay = Layout(n, heads, bq, bk)
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_every_element(case):
+    name, B, n, bq, bk, heads = case[:6]
+    lay = Layout(n, heads, bq, bk, split_keys=case[6] if len(case) > 6 else 0)
+    if name.startswith("split"):
+        assert lay.header.comb_sched_len > 0
     inp = W.make_inputs(B, len(heads), n, 64, seed=zlib.crc32(name.encode()) % 10000)
     _check_dense(lay, heads, B, n, inp)
 
@@ -78,7 +82,7 @@ def test_fp32_forward_small_ragged():
 
 def test_fp32_forward_split_rows():
     heads = [HeadPattern("local", 1100), HeadPattern("stride", 2)]
-    lay = Layout(1100, heads, 64, 32)
+    lay = Layout(1100, heads, 64, 32, split_keys=1024)
     assert lay.header.comb_sched_len > 0
     inp = W.make_inputs(1, 2, 1100, 64, seed=6, dtype="fp32")
     _check_dense(lay, heads, 1, 1100, inp, backward=False, fp32=True)
@@ -109,15 +113,37 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_repeat_calls_are_bitwise_deterministic():
-    """No atomics anywhere: forward and backward reproduce bit for bit (split key tiles included)."""
+    """No atomics; split tiles are merged in chunk order: forward and backward reproduce
+    bit for bit, with the same workspaces reused across calls."""
     heads = [HeadPattern("sameblock", 64), HeadPattern("summary", 64, 16, 0)]
-    lay = Layout(4096, heads, 64, 64)
-    assert lay.header.num_slots > 0  # some key tiles are split into chunks
+    lay = Layout(4096, heads, 64, 64, split_keys=512)
+    h = lay.header
+    assert h.num_slots > 0 and h.num_qslots > 0  # split key and query tiles
     inp = W.make_inputs(1, 2, 4096, 64, seed=77)
-    a = run_gpu(lay, inp, True)
-    b = run_gpu(lay, inp, True)
-    for key in ("o", "lse", "dq", "dk", "dv"):
-        assert np.array_equal(a[key], b[key]), key
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    fws = torch.empty(bd.fwd_workspace_bytes(lay, 1, 2), dtype=torch.uint8, device=dev)
+    bws = torch.empty(bd.bwd_workspace_bytes(lay, 1, 2), dtype=torch.uint8, device=dev)
+    runs = []
+    for _ in range(3):
+        o, lse = bd.sparse_attn_fwd(lay, q, k, v, workspace=fws)
+        grads = bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=bws)
+        torch.cuda.synchronize()
+        runs.append([to64(t) for t in (o, lse, *grads)])
+    for r in runs[1:]:
+        for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), runs[0], r):
+            assert np.array_equal(x, y), name
+
+
+def test_many_chunks_per_tile_every_element():
+    """Small chunk caps: up to a dozen chunks per split tile."""
+    heads = [HeadPattern("local", 600), HeadPattern("summary", 32, 8, 1), HeadPattern("stride", 3)]
+    n, B = 700, 2
+    lay = Layout(n, heads, 32, 32, split_keys=64, split_rows=64)
+    fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
+    assert max(fs[:, 7]) >= 8 and max(bs[:, 7]) >= 8
+    inp = W.make_inputs(B, len(heads), n, 64, seed=4242)
+    _check_dense(lay, heads, B, n, inp)
 
 
 def test_masked_value_perturbation_on_gpu():

@@ -123,11 +123,12 @@ def test_schedules_cover_every_tile_heaviest_first():
     h = lay.header
     fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
     fwork, bwork = [], []
-    for head, qt, e0, e1, slot in fs:
+    for head, qt, e0, e1, slot, group, slot0, nch in fs:
+        assert (group, slot0, nch) == (-1, -1, 1)
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
         assert (e0, e1, slot) == (a["row_ptr"][qt], a["row_ptr"][qt + 1], -1)  # no split at n=1000
         fwork.append(e1 - e0)
-    for head, kt, e0, e1, slot in bs:
+    for head, kt, e0, e1, slot, group, slot0, nch in bs:
         bwork.append(e1 - e0)
     assert all(w > 0 for w in fwork)
     assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
@@ -196,6 +197,9 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
             else:
                 s0, nch = red[(head, kt)]
                 assert [r[2] for r in rows] == list(range(s0, s0 + nch))
+                grp = {(int(r[5]), int(r[6]), int(r[7])) for r in bs if r[0] == head and r[1] == kt}
+                gidx = [i for i, r in enumerate(rs) if (r[0], r[1]) == (head, kt)]
+                assert grp == {(gidx[0], s0, nch)}
     if n == 12288:
         assert h.red_sched_len > 0 and h.num_slots > h.red_sched_len
 
@@ -209,11 +213,11 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
 ])
 def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
     """Each query tile's CSR list is covered exactly once by forward / dQ items, in
-    contiguous chunks of at most 1024 keys; split tiles own consecutive slots that
-    the combine schedule lists."""
+    contiguous chunks of at most split_keys (default 2048) keys; split tiles own
+    consecutive slots that the merge schedule lists."""
     lay = Layout(n, heads, bq, bk)
     h = lay.header
-    assert h.split_keys == 1024
+    assert h.split_keys == 2048
     qcap = max(1, h.split_keys // bk)
     fs, cs = lay.fwd_schedule(), lay.combine_schedule()
     slots = sorted(int(r[4]) for r in fs if r[4] >= 0)
@@ -237,6 +241,9 @@ def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
                 s0, nch = comb[(head, qt)]
                 assert nch == -(-(r1 - r0) // qcap)
                 assert [r[2] for r in rows] == list(range(s0, s0 + nch))
+                grp = {(int(r[5]), int(r[6]), int(r[7])) for r in fs if r[0] == head and r[1] == qt}
+                gidx = [i for i, r in enumerate(cs) if (r[0], r[1]) == (head, qt)]
+                assert grp == {(gidx[0], s0, nch)}
     if n == 12288:
         # summary heads read up to 3072 keys per row; strided heads stay within one class
         assert (h.comb_sched_len > 0) == any(p.kind == "summary" for p in heads)
@@ -400,9 +407,6 @@ def test_fwd_bwd_argument_errors_before_any_launch():
                                          kw.get("H", 2), kw.get("d", 64), kw.get("dt", 0), fake,
                                          fake, fake, kw.get("o", fake), fake, kw.get("ws", fake),
                                          kw.get("wsb", 1 << 30), kw.get("scale", 0.0), None)
-    fp = lambda ph: lib.sparse_attn_fwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake,
-                                               fake, 1 << 30, 0.0, ph, None)
-    assert fp(0) == bd.SA_EINVAL and fp(4) == bd.SA_EINVAL
     assert f(blob=None) == bd.SA_EINVAL
     assert f(H=3) == bd.SA_EINVAL
     assert f(B=-1) == bd.SA_EINVAL
@@ -422,6 +426,7 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert lib.sparse_attn_fwd_workspace(big.blob.ctypes.data, 3, 2, 64, 0, ctypes.byref(size)) == 0
     rows = 3 * big.header.num_qslots * 64
     rnd = lambda x: -(-x // 256) * 256
+    # partial O, partial max, partial sum
     assert size.value == rnd(rows * 64 * 4) + 2 * rnd(rows * 4)
     hbig = big.blob.ctypes.data
     assert lib.sparse_attn_fwd(hbig, fake, 3, 2, 64, 0, fake, fake, fake, fake, fake, fake,
@@ -437,3 +442,15 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert g(ws=16) == bd.SA_ESIZE
     assert g(dt=1) == bd.SA_EUNSUPPORTED
     assert g(B=0) == bd.SA_OK
+    gp = lambda ph: lib.sparse_attn_bwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake, fake,
+                                               fake, fake, fake, fake, 1 << 30, 0.0, ph, None)
+    assert gp(0) == bd.SA_EINVAL and gp(8) == bd.SA_EINVAL
+    fp = lambda ph: lib.sparse_attn_fwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake,
+                                               fake, 1 << 30, 0.0, ph, None)
+    assert fp(0) == bd.SA_EINVAL and fp(4) == bd.SA_EINVAL
+    # split key and query tiles: D, dK/dV partials, dQ partials
+    assert lib.sparse_attn_bwd_workspace(hbig, 3, 2, 64, 0, ctypes.byref(size)) == 0
+    hdr = big.header
+    assert hdr.red_sched_len > 0 and hdr.comb_sched_len > 0
+    assert size.value == (rnd(3 * 2 * 12288 * 4) + rnd(3 * hdr.num_slots * 2 * 64 * 64 * 4)
+                          + rnd(3 * hdr.num_qslots * 64 * 64 * 4))
