@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--workloads", default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the workloads, run one device-to-device copy of this many MiB "
+                         "(a plain copy kernel of known size, for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -156,6 +159,14 @@ def main():
     from factorized_block_sparse_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     names = [s for s in args.workloads.split(",") if s]
     wls = [W.WORKLOADS[nm] for nm in names]
     inputs, runs = {}, []

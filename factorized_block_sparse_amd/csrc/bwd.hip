@@ -69,11 +69,10 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
-  constexpr int KS = kD + 8;   // row stride of K, V in LDS
-  constexpr int CPT = BK * 8 / NT;
-  static_assert(CPT >= 1 && (BK * 8) % NT == 0, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * KS];
+  constexpr int IPW = BK / 8 / NW;  // 1 KB direct loads per wave, tensor and tile
+  static_assert(IPW >= 1 && (BK / 8) % NW == 0, "tile/wave mismatch");
+  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * kD];  // swizzled tiles
+  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -110,55 +109,51 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
       dof[c] = bf16x8{};
     }
   }
-  dsum += other_half(dsum);
+  dsum = pair_sum(dsum);
   if (tok >= 0 && g == 0) p.dsum[base + tok] = dsum;
+  floatx16 ndv;  // -D of the lane's row in every register: seeds the dP accumulator
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndv[r] = -dsum;
 
-  u32x4 kreg[CPT], vreg[CPT];
-  int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
+  // K, V tiles by direct loads, as in the forward; padding keys fetch token 0
+  // (never visible: their probabilities, hence dS, are exactly 0).
+  const bf16* kg = p.k + base * kD;
+  const bf16* vg = p.v + base * kD;
+  const int drow = lane >> 3;
+  const int dcol = ((lane & 7) ^ drow) * 8;
+  int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) kidx[i] = pv.kmap[kt * BK + ((tid + i * NT) >> 3)];
+    for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
   };
-  auto gload = [&]() {
+  auto dload = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cc = (tid + i * NT) & 7;
-      const int tk = kidx[i];
-      if (tk >= 0) {
-        kreg[i] = reinterpret_cast<const u32x4*>(p.k + (base + tk) * kD)[cc];
-        vreg[i] = reinterpret_cast<const u32x4*>(p.v + (base + tk) * kD)[cc];
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      *reinterpret_cast<u32x4*>(&ks[buf][j * KS + cc * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][j * KS + cc * 8]) = vreg[i];
+    for (int i = 0; i < IPW; ++i) {
+      const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
+      dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
+      dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
     }
   };
 
   floatx16 dqa[2];
   dqa[0] = dqa[1] = floatx16{};
   const float c2 = p.scale_log2;
+  TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
-    iload(pv.col[e0]);
-    gload();
-    lstore(0);
-    if (e0 + 1 < e1) iload(pv.col[e0 + 1]);
+    iload(win.get(e0) >> 1);
+    dload(0);
+    if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }
+  wait_vmem();
   __syncthreads();
   for (int it = e0; it < e1; ++it) {
     const int buf = (it - e0) & 1;
-    const int kt = pv.col[it];
-    const bool full = pv.fflag[it] == SA_TILE_FULL;
+    const int ent = win.get(it);
+    const int kt = ent >> 1;
+    const bool full = (ent & 1) != 0;
     if (it + 1 < e1) {
-      gload();                                   // tile it+1, indices already here
-      if (it + 2 < e1) iload(pv.col[it + 2]);    // indices of tile it+2
+      dload(buf ^ 1);                                  // tile it+1, indices already here
+      if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
     const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
@@ -168,12 +163,13 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
       constexpr bool IS_FULL = decltype(full_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        floatx16 s = floatx16{}, dp = floatx16{};
-        const int roff = (32 * kb + sigma32(l32)) * KS + 8 * g;
+        floatx16 s = floatx16{}, dp = ndv;  // dp accumulates dP - D
+        const int kr = 32 * kb + sigma32(l32);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][roff + 16 * c]), qf[c], s);
-          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[buf][roff + 16 * c]), dof[c], dp);
+          const int off = swz(kr, g + 2 * c);
+          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][off]), qf[c], s);
+          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[buf][off]), dof[c], dp);
         }
         // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
         const int lo_rel = lo - k0 - 32 * kb - 8 * g, hi_rel = hi - k0 - 32 * kb - 8 * g;
@@ -185,14 +181,14 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
             const int cr = 16 * (r >> 3) + (r & 7);  // key offset beyond 32*kb + 8*g
             pr = (cr >= lo_rel && cr <= hi_rel) ? pr : 0.f;
           }
-          ds[r] = pr * (dp[r] - dsum);
+          ds[r] = pr * dp[r];
         }
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
           const bf16x8 db = pack_bf16x8(&ds[8 * h8]);
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
-            dqa[fb] = mfma_bf16(load_a_transposed(ks[buf], KS, 32 * kb + 16 * h8, 32 * fb, lane),
+            dqa[fb] = mfma_bf16(load_a_transposed_swz(ks[buf], 32 * kb + 16 * h8, 32 * fb, lane),
                                 db, dqa[fb]);
         }
       }
@@ -203,7 +199,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
       else
         tile(std::false_type{});
     }
-    if (it + 1 < e1) lstore(buf ^ 1);
+    wait_vmem();  // tile it+1 is in LDS (this wave's part)
     __syncthreads();
   }
 
@@ -252,15 +248,15 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QS = BQ < 64 ? BQ : 64;
   constexpr int NSTEP = BQ / QS;
   constexpr int NQB = QS / 32;
-  constexpr int RS = kD + 8;  // row stride of Q / dO in LDS
-  constexpr int CPT = QS * 8 / NT;
-  static_assert(CPT >= 1 && (QS * 8) % NT == 0, "tile/wave mismatch");
+  constexpr int IPW = QS / 8 / NW;  // 1 KB direct loads per wave, tensor and step
+  static_assert(IPW >= 1 && (QS / 8) % NW == 0, "tile/wave mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 sq[2][QS * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sdo[2][QS * RS];
-  // (LSE * log2(e), D) of each staged query row, interleaved so that the
-  // values of 8 consecutive rows are four 16-byte reads.
-  __shared__ __attribute__((aligned(16))) float smeta[2][2 * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sq[2][QS * kD];  // swizzled tiles
+  __shared__ __attribute__((aligned(16))) bf16 sdo[2][QS * kD];
+  // LSE * log2(e) and -D of each staged query row.  -D seeds the dP
+  // accumulator (the MFMA then yields dP - D directly).
+  __shared__ __attribute__((aligned(16))) float slse[2][QS];
+  __shared__ __attribute__((aligned(16))) float snd[2][QS];
   __shared__ __attribute__((aligned(16))) int32_t slo[2][QS];
   __shared__ __attribute__((aligned(16))) int32_t shi[2][QS];
 
@@ -297,53 +293,48 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const int nsteps = (c1 - c0) * NSTEP;
   const float c2 = p.scale_log2;
 
-  u32x4 qreg[CPT], doreg[CPT];
+  // Q, dO rows by direct loads (swizzled tiles); per-row LSE, D and key
+  // intervals through registers.  Padding query rows fetch token 0 and get
+  // LSE = +inf, so their probabilities (hence dS) are exactly 0.
+  const bf16* qgl = p.q + base * kD;
+  const bf16* dgl = p.dout + base * kD;
+  const int drow = lane >> 3;
+  const int dcol = ((lane & 7) ^ drow) * 8;
   float lse_r = 0.f, dd_r = 0.f;
   int lo_r = 1, hi_r = 0;
-  int qidx[CPT], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
+  int qidx[IPW], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
+  TileWindow win = tile_window(pv.row, pv.bflag, c0, c1);
   auto iload = [&](int step) {
-    const int e = c0 + step / NSTEP;
-    const int r0 = pv.row[e] * BQ + (step % NSTEP) * QS;
+    const int r0 = (win.get(c0 + step / NSTEP) >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) qidx[i] = pv.qmap[r0 + ((tid + i * NT) >> 3)];
+    for (int i = 0; i < IPW; ++i) qidx[i] = pv.qmap[r0 + 8 * (w * IPW + i) + drow];
     if (tid < QS) rtok = pv.qmap[r0 + tid];
   };
-  auto gload = [&](int step) {
-    const int e = c0 + step / NSTEP;
-    const int r0 = pv.row[e] * BQ + (step % NSTEP) * QS;
+  auto gload = [&](int step, int buf) {
+    const int ent = win.get(c0 + step / NSTEP);
+    const int r0 = (ent >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cc = (tid + i * NT) & 7;
-      const int tk = qidx[i];
-      if (tk >= 0) {
-        qreg[i] = reinterpret_cast<const u32x4*>(p.q + (base + tk) * kD)[cc];
-        doreg[i] = reinterpret_cast<const u32x4*>(p.dout + (base + tk) * kD)[cc];
-      } else {
-        qreg[i] = u32x4{0u, 0u, 0u, 0u};
-        doreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < IPW; ++i) {
+      const size_t off = size_t(qidx[i] < 0 ? 0 : qidx[i]) * kD + dcol;
+      dma16(qgl + off, &sq[buf][8 * (w * IPW + i) * kD]);
+      dma16(dgl + off, &sdo[buf][8 * (w * IPW + i) * kD]);
     }
     if (tid < QS) {
       const int r = r0 + tid;
       const int tk = rtok;
       // Row intervals are read only by the masked body (PARTIAL tiles).
-      if (pv.bflag[e] != SA_TILE_FULL) {
+      if ((ent & 1) == 0) {
         lo_r = pv.lo[r];
         hi_r = pv.hi[r];
       }
-      lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : 0.f;
+      lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : INFINITY;
       dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      *reinterpret_cast<u32x4*>(&sq[buf][j * RS + cc * 8]) = qreg[i];
-      *reinterpret_cast<u32x4*>(&sdo[buf][j * RS + cc * 8]) = doreg[i];
-    }
+  auto mstore = [&](int buf) {
     if (tid < QS) {
-      *reinterpret_cast<floatx2*>(&smeta[buf][2 * tid]) = floatx2{lse_r, dd_r};
+      slse[buf][tid] = lse_r;
+      snd[buf][tid] = -dd_r;
       slo[buf][tid] = lo_r;
       shi[buf][tid] = hi_r;
     }
@@ -351,31 +342,39 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   if (nsteps > 0) {
     iload(0);
-    gload(0);
-    lstore(0);
+    gload(0, 0);
     if (nsteps > 1) iload(1);
   }
+  wait_vmem();
+  mstore(0);
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    if (step + 1 < nsteps) {
-      gload(step + 1);                       // indices already here
-      if (step + 2 < nsteps) iload(step + 2);
-    }
-
     // PARTIAL tiles set hidden scores to -inf (probability 0) under one
     // uniform branch; FULL tiles (every pair visible) skip it.
-    const bool full = pv.bflag[c0 + step / NSTEP] == SA_TILE_FULL;
+    const bool full = (win.get(c0 + step / NSTEP) & 1) != 0;
+    if (step + 1 < nsteps) {
+      gload(step + 1, buf ^ 1);               // indices already here
+      if (step + 2 < nsteps) iload(step + 2);
+    }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      floatx16 s = floatx16{}, dp = floatx16{};
-      const int roff = (32 * qb + sigma32(l32)) * RS + 8 * g;
+      // Register r of half g: query 32*qb + kappa(r, g); lane = key.  Registers
+      // 0..7 are rows 32*qb + 8*g + 0..7, registers 8..15 the same + 16.
+      const int qa = 32 * qb + 8 * g;
+      const floatx4* nd0 = reinterpret_cast<const floatx4*>(&snd[buf][qa]);
+      const floatx4* nd1 = reinterpret_cast<const floatx4*>(&snd[buf][qa + 16]);
+      const floatx4 n0 = nd0[0], n1 = nd0[1], n2 = nd1[0], n3 = nd1[1];
+      floatx16 s = floatx16{};
+      floatx16 dp = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                     n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+      const int qr = 32 * qb + sigma32(l32);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[buf][roff + 16 * c]), kq[c], s);
-        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[buf][roff + 16 * c]), vq[c], dp);
+        const int off = swz(qr, g + 2 * c);
+        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[buf][off]), kq[c], s);
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[buf][off]), vq[c], dp);
       }
-      // Register r of half g: query 32*qb + kappa(r, g); lane = key.
       if (!full) {
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
@@ -397,18 +396,15 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const int qloc = 32 * qb + 16 * h8 + 8 * g;
-        const floatx4* mp = reinterpret_cast<const floatx4*>(&smeta[buf][2 * qloc]);
-        const floatx4 m0 = mp[0], m1 = mp[1], m2 = mp[2], m3 = mp[3];
-        const float mv[16] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3],
-                              m2[0], m2[1], m2[2], m2[3], m3[0], m3[1], m3[2], m3[3]};
+        const floatx4 la = *reinterpret_cast<const floatx4*>(&slse[buf][qloc]);
+        const floatx4 lb = *reinterpret_cast<const floatx4*>(&slse[buf][qloc + 4]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * h8 + j;
-          const float l2 = mv[2 * j];
-          const float dd = mv[2 * j + 1];
+          const float l2 = j < 4 ? la[j] : lb[j - 4];
           const float pp = fast_exp2(fmaf(s[r], c2, -l2));
           pr[r] = pp;
-          ds[r] = pp * (dp[r] - dd);
+          ds[r] = pp * dp[r];  // dp holds dP - D
         }
       }
 #pragma unroll
@@ -418,12 +414,13 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
           const int q0 = 32 * qb + 16 * h8;
-          dva[fb] = mfma_bf16(load_a_transposed(sdo[buf], RS, q0, 32 * fb, lane), pb, dva[fb]);
-          dka[fb] = mfma_bf16(load_a_transposed(sq[buf], RS, q0, 32 * fb, lane), sb, dka[fb]);
+          dva[fb] = mfma_bf16(load_a_transposed_swz(sdo[buf], q0, 32 * fb, lane), pb, dva[fb]);
+          dka[fb] = mfma_bf16(load_a_transposed_swz(sq[buf], q0, 32 * fb, lane), sb, dka[fb]);
         }
       }
     }
-    if (step + 1 < nsteps) lstore(buf ^ 1);
+    wait_vmem();  // step+1 staged (this wave's part)
+    if (step + 1 < nsteps) mstore(buf ^ 1);
     __syncthreads();
   }
 

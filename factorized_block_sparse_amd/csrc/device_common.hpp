@@ -82,8 +82,67 @@ __device__ __forceinline__ bf16x8 load_a_transposed(const bf16* m, int stride, i
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-// Value of lane L ^ 32 (the other half of the wave).
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles filled by direct global->LDS loads.
+//
+// A tile is row-major [rows][64] bf16 (128 bytes per row, no padding); the
+// eight 16-byte chunks of row r are stored XOR-swizzled, logical chunk c at
+// physical chunk c ^ (r & 7), so that reads of one chunk column over eight
+// consecutive rows hit eight different bank groups.
+//
+// The gfx950 16-byte global->LDS load writes lane L's 16 bytes to
+// lds_base + 16 L (lds_base wave-uniform): one instruction fills a 1 KB block
+// = 8 rows.  Lane L therefore fetches row (L / 8) of its block, logical chunk
+// (L % 8) ^ (L / 8).  The loads count on vmcnt; wait_vmem() before the
+// barrier that publishes the tile.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kD + ((chunk ^ (row & 7)) << 3);
+}
+
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every global load of this wave (direct-to-LDS included)
+// has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposed A operand (see load_a_transposed) from a swizzled tile.
+__device__ __forceinline__ bf16x8 load_a_transposed_swz(const bf16* m, int k0, int c0, int lane) {
+  const int g = lane >> 5, q = (lane >> 4) & 1, j = lane & 15;
+  const int t = j & 3;
+  const int tsw = ((t & 1) << 1) | (t >> 1);
+  const int col = c0 + 16 * q + 4 * tsw;  // multiple of 4: half of a 16-byte chunk
+  const int r0 = k0 + 8 * g + (j >> 2), r1 = r0 + 4;
+  const v4i16 a = lds_read_tr16(m + swz(r0, col >> 3) + (col & 7));
+  const v4i16 b = lds_read_tr16(m + swz(r1, col >> 3) + (col & 7));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Combining a value with the one in lane L ^ 32 (the other half of the
+// wave) through v_permlane32_swap (gfx950): swapping lanes 32..63 of one copy
+// with lanes 0..31 of another leaves every lane holding (x[L % 32],
+// x[L % 32 + 32]); one VALU exchange instead of an LDS permute.
+__device__ __forceinline__ void halves(float x, float* lo, float* hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  *lo = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+  *hi = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+// max / sum of x over lanes L and L ^ 32 (the same value in both lanes).
+__device__ __forceinline__ float pair_max(float x) {
+  float lo, hi;
+  halves(x, &lo, &hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float lo, hi;
+  halves(x, &lo, &hi);
+  return lo + hi;
+}
 
 // Two floats -> two bf16 packed in 32 bits, round-to-nearest-even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -134,6 +193,40 @@ __device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head
   v.row = reinterpret_cast<const int32_t*>(blob + rec->row_off);
   v.bflag = blob + rec->bflag_off;
   return v;
+}
+
+// A wave's register window over a tile list (CSR or CSC entries [e0, e1)):
+// lane l holds entry base + l packed as (tile << 1) | FULL, so the loop reads
+// an entry with one readlane instead of a global load whose latency would
+// stall the prefetch issued before it (the vector-memory counter drains in
+// order).  A loop may read up to two entries ahead of the one it works on:
+// entries are requested in non-decreasing order apart from that look-ahead,
+// and a window that has to advance starts two entries before the requested
+// one, so the entries still in use stay inside it.
+struct TileWindow {
+  const int32_t* tile;
+  const uint8_t* flag;
+  int e1, base, packed;
+  __device__ __forceinline__ void load(int b) {
+    const int e = b + int(__lane_id());
+    base = b;
+    packed = e < e1 ? (tile[e] << 1) | (flag[e] == SA_TILE_FULL ? 1 : 0) : 0;
+  }
+  // Entry e (uniform, e >= base); moves the window forward when e is past it.
+  __device__ __forceinline__ int get(int e) {
+    if (e >= base + 64) load(e - 2);
+    return __builtin_amdgcn_readlane(packed, e - base);
+  }
+};
+
+__device__ __forceinline__ TileWindow tile_window(const int32_t* tile, const uint8_t* flag,
+                                                  int e0, int e1) {
+  TileWindow w;
+  w.tile = tile;
+  w.flag = flag;
+  w.e1 = e1;
+  w.load(e0);
+  return w;
 }
 
 // Workgroup -> (batch element, schedule entry) through the per-XCD lists of

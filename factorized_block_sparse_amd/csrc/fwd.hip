@@ -5,18 +5,21 @@
 // ("Sparse Transformers 深度解读报告", section 3.5: blocked sub-blocks of
 // Q/K/V, the softmax fused into a single kernel with its intermediates in
 // registers, masked-out tiles never computed).  Per key tile:
-//   1. K and V rows (through the pattern's key map) are staged into LDS
-//      row-major, double-buffered, one barrier per tile; V^T reaches the MFMA
-//      through transposing LDS reads;
+//   1. K and V rows (through the pattern's key map) are copied straight from
+//      global memory into LDS (direct loads, no registers), row-major with
+//      XOR-swizzled 16-byte chunks, double-buffered, one barrier per tile;
+//      V^T reaches the MFMA through transposing LDS reads;
 //   2. each wave owns 32 query rows and computes S^T = K Q^T on the MFMA
 //      units (fp32 accumulation; Q stays in registers for the whole walk);
 //   3. on PARTIAL tiles the fine mask is two integer compares against the
 //      row's key interval; FULL tiles apply no mask;
-//   4. running max / sum update in base 2 with the softmax scale folded into
-//      one FMA per score; the running max (and the rescale of the output
-//      accumulator) only moves when a tile's max exceeds it by more than
-//      2^kRescaleLog2, so P <= 2^kRescaleLog2 and most tiles skip the rescale;
-//   5. O^T += V^T P^T on the MFMA units, P rounded to the input type.
+//   4. running max update in base 2 with the softmax scale folded into one
+//      FMA per score; the running max (and the rescale of the accumulators)
+//      only moves when a tile's max exceeds it by more than 2^kRescaleLog2,
+//      so P <= 2^kRescaleLog2 and most tiles skip the rescale; the row max
+//      pairs the two half-waves through a lane swap;
+//   5. O^T += V^T P^T on the MFMA units, P rounded to the input type; the
+//      row sums accumulate the unrounded P in float32.
 // The epilogue writes O rows (through the query map) and the per-row
 // log-sum-exp that the backward pass rebuilds probabilities from (report
 // section 3.4).  A wave skips the arithmetic of a tile none of its rows can
@@ -95,13 +98,13 @@ __device__ __forceinline__ void fwd_merge_row(const FwdParams& p, const PatView&
 }
 
 // Epilogue shared by both element types.  Register r of half g of oacc[fb]
-// holds feature 32*fb + kappa(r, g) of the lane's query row.  Unsplit tiles
+// holds feature 32*fb + kappa(r, g) of the lane's query row; l_tot is the
+// row's full sum of probabilities.  Unsplit tiles
 // write O = acc / l and LSE; chunks of split tiles store (acc, m, l).
 template <typename T, int BQ>
 __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 (&oacc)[2],
-                                             float m_run, float l_run, int tok, size_t base,
+                                             float m_run, float l_tot, int tok, size_t base,
                                              int b, int slot, int row, int g) {
-  const float l_tot = l_run + other_half(l_run);
   if (slot < 0) {
     if (tok < 0) return;
     const float inv = 1.0f / l_tot;
@@ -148,13 +151,11 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 
 template <int BQ, int BK>
 __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
-  constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
-  constexpr int KS = kD + 8;  // LDS row stride of K and V (elements)
-  constexpr int CPT = BK * 8 / NT;  // 16-byte chunks per thread and tensor
-  static_assert(CPT >= 1 && (BK * 8) % NT == 0, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * KS];
+  constexpr int IPW = BK / 8 / NW;  // 1 KB direct loads per wave, tensor and tile
+  static_assert(IPW >= 1 && (BK / 8) % NW == 0, "tile/wave mismatch");
+  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * kD];
+  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -182,55 +183,47 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
     for (int c = 0; c < 4; ++c) qf[c] = bf16x8{};
   }
 
-  u32x4 kreg[CPT], vreg[CPT];
-  int kidx[CPT];  // key-map entries of the next tile to load (fetched a tile early)
+  // Staging of K and V tiles: wave w fills rows [8 (w IPW + i), +8) of each
+  // tile with its i-th direct load.  Padding keys (map entry -1) fetch token
+  // 0 instead: they are never visible, so their probabilities are exactly 0.
+  const int drow = lane >> 3;
+  const int dcol = ((lane & 7) ^ drow) * 8;  // element offset of the fetched chunk
+  int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) kidx[i] = pv.kmap[kt * BK + ((tid + i * NT) >> 3)];
+    for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
   };
-  auto gload = [&]() {
+  auto dload = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cc = (tid + i * NT) & 7;
-      const int tk = kidx[i];
-      if (tk >= 0) {
-        kreg[i] = reinterpret_cast<const u32x4*>(kg + size_t(tk) * kD)[cc];
-        vreg[i] = reinterpret_cast<const u32x4*>(vg + size_t(tk) * kD)[cc];
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT, j = c >> 3, cc = c & 7;
-      *reinterpret_cast<u32x4*>(&ks[buf][j * KS + cc * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][j * KS + cc * 8]) = vreg[i];
+    for (int i = 0; i < IPW; ++i) {
+      const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
+      dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
+      dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
     }
   };
 
   floatx16 oacc[2];
   oacc[0] = floatx16{};
   oacc[1] = floatx16{};
-  float m_run = kNegInit, l_run = 0.f;
+  float m_run = kNegInit, l_run = 0.f;  // l_run: this half-wave's share of the row sum
   const float c2 = p.scale_log2;
 
+  TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
-    iload(pv.col[e0]);
-    gload();
-    lstore(0);
-    if (e0 + 1 < e1) iload(pv.col[e0 + 1]);
+    iload(win.get(e0) >> 1);
+    dload(0);
+    if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }
+  wait_vmem();
   __syncthreads();
   for (int it = e0; it < e1; ++it) {
     const int buf = (it - e0) & 1;
-    const int kt = pv.col[it];
-    const bool full = pv.fflag[it] == SA_TILE_FULL;
+    const int ent = win.get(it);
+    const int kt = ent >> 1;
+    const bool full = (ent & 1) != 0;
     if (it + 1 < e1) {
-      gload();                                   // tile it+1, indices already here
-      if (it + 2 < e1) iload(pv.col[it + 2]);    // indices of tile it+2
+      dload(buf ^ 1);                                  // tile it+1, indices already here
+      if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
     const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
@@ -239,10 +232,11 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = floatx16{};
-        const bf16* krow = &ks[buf][(32 * kb + sigma32(l32)) * KS + 8 * g];
+        const int kr = 32 * kb + sigma32(l32);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          s[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(krow + 16 * c), qf[c], s[kb]);
+          s[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][swz(kr, g + 2 * c)]), qf[c],
+                            s[kb]);
       }
       if (!full) {
         // Key k0 + c is visible iff lo <= k0 + c <= hi; c = 32*kb + kappa(r, g)
@@ -261,7 +255,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, other_half(mx)) * c2;
+      mx = pair_max(mx) * c2;
       if (__any(mx > m_run + kRescaleLog2)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
@@ -278,9 +272,8 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(fmaf(s[kb][r], c2, -m_run));
-          s[kb][r] = pr;
-          lsum += pr;
+          s[kb][r] = fast_exp2(fmaf(s[kb][r], c2, -m_run));
+          lsum += s[kb][r];
         }
       l_run += lsum;
 #pragma unroll
@@ -293,16 +286,16 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
           const bf16x8 pb = pack_bf16x8(tmp);
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
-            oacc[fb] = mfma_bf16(load_a_transposed(vs[buf], KS, 32 * kb + 16 * h8, 32 * fb, lane),
+            oacc[fb] = mfma_bf16(load_a_transposed_swz(vs[buf], 32 * kb + 16 * h8, 32 * fb, lane),
                                  pb, oacc[fb]);
         }
       }
     }
-    if (it + 1 < e1) lstore(buf ^ 1);
+    wait_vmem();  // tile it+1 is in LDS (this wave's part)
     __syncthreads();
   }
 
-  fwd_epilogue<bf16, BQ>(p, oacc, m_run, l_run, tok, base, b, it8[4], w * 32 + l32, g);
+  fwd_epilogue<bf16, BQ>(p, oacc, m_run, pair_sum(l_run), tok, base, b, it8[4], w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------
@@ -402,7 +395,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
           s[kb][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, other_half(mx));
+      mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
       float lsum = 0.f;
@@ -435,7 +428,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  fwd_epilogue<float, BQ>(p, oacc, m_run, l_run, tok, base, b, it8[4], w * 32 + l32, g);
+  fwd_epilogue<float, BQ>(p, oacc, m_run, pair_sum(l_run), tok, base, b, it8[4], w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------

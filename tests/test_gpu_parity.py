@@ -135,6 +135,20 @@ def test_repeat_calls_are_bitwise_deterministic():
             assert np.array_equal(x, y), name
 
 
+def test_unsplit_long_tile_lists_every_element():
+    """Splitting off: CSR and CSC lists of well over 64 tiles (the kernels walk them
+    through 64-entry register windows)."""
+    heads = [HeadPattern("local", 4800), HeadPattern("summary", 64, 16, 0)]
+    n = 5000
+    lay = Layout(n, heads, 32, 32, split_keys=1 << 30, split_rows=1 << 30)
+    h = lay.header
+    assert h.comb_sched_len == 0 and h.red_sched_len == 0
+    fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
+    assert max(fs[:, 3] - fs[:, 2]) > 128 and max(bs[:, 3] - bs[:, 2]) > 128
+    inp = W.make_inputs(1, len(heads), n, 64, seed=9090)
+    _check_dense(lay, heads, 1, n, inp)
+
+
 def test_many_chunks_per_tile_every_element():
     """Small chunk caps: up to a dozen chunks per split tile."""
     heads = [HeadPattern("local", 600), HeadPattern("summary", 32, 8, 1), HeadPattern("stride", 3)]
