@@ -71,6 +71,7 @@ class CBlobHeader(ctypes.Structure):
                 ("num_slots", ctypes.c_int32),
                 ("fwd_xl_off", ctypes.c_int64), ("bwd_xl_off", ctypes.c_int64),
                 ("fwd_xl_len", ctypes.c_int32), ("bwd_xl_len", ctypes.c_int32),
+                ("fwd_xitem_off", ctypes.c_int64), ("bwd_xitem_off", ctypes.c_int64),
                 ("comb_sched_off", ctypes.c_int64), ("comb_sched_len", ctypes.c_int32),
                 ("num_qslots", ctypes.c_int32),
                 ("split_keys", ctypes.c_int32), ("split_rows", ctypes.c_int32),
@@ -219,8 +220,9 @@ class Layout:
         }
 
     def fwd_schedule(self) -> np.ndarray:
-        """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot, merge group,
-        first slot of the group, chunks of the group); -1 / 1 for unsplit tiles."""
+        """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot, pattern index,
+        first slot of the tile, chunks of the tile); slot = slot0 = -1, chunks = 1 for
+        unsplit tiles."""
         return self._arr(self.header.fwd_sched_off, SA_SCHED_FIELDS * self.header.fwd_sched_len,
                          np.int32).reshape(-1, SA_SCHED_FIELDS)
 
@@ -232,6 +234,12 @@ class Layout:
         """Rows as fwd_schedule over (head, k-tile) and CSC entries."""
         return self._arr(self.header.bwd_sched_off, SA_SCHED_FIELDS * self.header.bwd_sched_len,
                          np.int32).reshape(-1, SA_SCHED_FIELDS)
+
+    def xcd_items(self, which: str) -> np.ndarray:
+        """[SA_XCDS, len, SA_SCHED_FIELDS] schedule entries in list order ("fwd" or "bwd")."""
+        h = self.header
+        off, ln = (h.fwd_xitem_off, h.fwd_xl_len) if which == "fwd" else (h.bwd_xitem_off, h.bwd_xl_len)
+        return self._arr(off, SA_XCDS * ln * SA_SCHED_FIELDS, np.int32).reshape(SA_XCDS, ln, SA_SCHED_FIELDS)
 
     def xcd_lists(self, which: str) -> np.ndarray:
         """[SA_XCDS, len] schedule indices per XCD ("fwd" or "bwd"), -1 = padding."""

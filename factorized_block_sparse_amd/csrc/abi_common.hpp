@@ -14,7 +14,7 @@ struct LaunchInfo {
   int32_t block_q, block_k, num_heads, n_pad, nqt, nkt;
   int32_t fwd_sched_len, bwd_sched_len;
   int64_t fwd_sched_off, bwd_sched_off, total_bytes;
-  int64_t fwd_xl_off, bwd_xl_off;
+  int64_t fwd_xl_off, bwd_xl_off, fwd_xitem_off, bwd_xitem_off;
   int32_t fwd_xl_len, bwd_xl_len;
 };
 
@@ -52,7 +52,36 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   li->bwd_xl_off = h.bwd_xl_off;
   li->fwd_xl_len = h.fwd_xl_len;
   li->bwd_xl_len = h.bwd_xl_len;
+  li->fwd_xitem_off = h.fwd_xitem_off;
+  li->bwd_xitem_off = h.bwd_xitem_off;
   return SA_OK;
+}
+
+// Device addresses of the first kArgPatterns patterns' arrays (host side of
+// PatTable: offsets from the host blob, added to the device copy's address).
+template <typename Table>
+inline void fill_pattern_table(const void* blob_host, const void* blob_dev, Table* t) {
+  const uint8_t* hb = static_cast<const uint8_t*>(blob_host);
+  const uint8_t* db = static_cast<const uint8_t*>(blob_dev);
+  sa_blob_header h;
+  memcpy(&h, hb, sizeof(h));
+  const int np = h.num_patterns < kArgPatterns ? h.num_patterns : kArgPatterns;
+  memset(t, 0, sizeof(*t));
+  for (int i = 0; i < np; ++i) {
+    sa_pattern_rec r;
+    memcpy(&r, hb + h.pattern_off + i * sizeof(sa_pattern_rec), sizeof(r));
+    auto& v = t->pv[i];
+    v.qmap = reinterpret_cast<const int32_t*>(db + r.qmap_off);
+    v.kmap = reinterpret_cast<const int32_t*>(db + r.kmap_off);
+    v.lo = reinterpret_cast<const int32_t*>(db + r.lo_off);
+    v.hi = reinterpret_cast<const int32_t*>(db + r.hi_off);
+    v.row_ptr = reinterpret_cast<const int32_t*>(db + r.row_ptr_off);
+    v.col = reinterpret_cast<const int32_t*>(db + r.col_off);
+    v.fflag = db + r.fflag_off;
+    v.col_ptr = reinterpret_cast<const int32_t*>(db + r.col_ptr_off);
+    v.row = reinterpret_cast<const int32_t*>(db + r.row_off);
+    v.bflag = db + r.bflag_off;
+  }
 }
 
 // scale <= 0 selects 1/sqrt(d) (blog post on sliding windows, section 01).

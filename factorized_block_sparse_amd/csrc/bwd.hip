@@ -36,10 +36,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
   const uint8_t* blob;
-  const int32_t* qsched;    // query-tile entries (the forward schedule), SA_SCHED_FIELDS ints
-  const int32_t* ksched;    // key-tile entries, SA_SCHED_FIELDS ints
-  const int32_t* qxl;       // per-XCD lists over qsched
-  const int32_t* kxl;       // per-XCD lists over ksched
+  const int32_t* qitems;    // per-XCD lists of query-tile entries (the forward's)
+  const int32_t* kitems;    // per-XCD lists of key-tile entries
   int32_t qxl_len, kxl_len;
   int32_t B, H, n, num_slots, num_qslots;
   const int32_t* rsched;    // (head, k-tile, first slot, chunks) of each split key tile
@@ -59,6 +57,7 @@ struct BwdParams {
   float* part_dq;  // [B, num_qslots, BQ, 64]: dQ chunks of split query tiles
   float scale;
   float scale_log2;
+  PatTable pats;  // arrays of the first patterns (device addresses)
 };
 
 // --------------------------------------------------------------------------
@@ -76,11 +75,11 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  int b, item;
-  if (!xcd_work_item(p.qxl, p.qxl_len, p.B, &b, &item)) return;
-  const int32_t* it8 = p.qsched + SA_SCHED_FIELDS * item;
+  int b;
+  const int32_t* it8 = xcd_work_entry(p.qitems, p.qxl_len, p.B, &b);
+  if (!it8) return;
   const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3], slot = it8[4];
-  const PatView pv = pattern_of_head(p.blob, head);
+  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int prow = qt * BQ + w * 32 + l32;
@@ -262,11 +261,11 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  int b, item;
-  if (!xcd_work_item(p.kxl, p.kxl_len, p.B, &b, &item)) return;
-  const int32_t* it8 = p.ksched + SA_SCHED_FIELDS * item;
+  int b;
+  const int32_t* it8 = xcd_work_entry(p.kitems, p.kxl_len, p.B, &b);
+  if (!it8) return;
   const int head = it8[0], kt = it8[1], c0 = it8[2], c1 = it8[3], slot = it8[4];
-  const PatView pv = pattern_of_head(p.blob, head);
+  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int kpos = kt * BK + 32 * w + l32;
@@ -593,14 +592,13 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
 
   BwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
-  prm.qsched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
-  prm.ksched = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_sched_off);
+  prm.qitems = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xitem_off);
+  prm.kitems = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xitem_off);
+  fill_pattern_table(blob_host, blob_dev, &prm.pats);
   prm.num_qslots = h.num_qslots;
   prm.kgroups = h.red_sched_len;
   prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
   prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
-  prm.qxl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
-  prm.kxl = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xl_off);
   prm.qxl_len = li.fwd_xl_len;
   prm.kxl_len = li.bwd_xl_len;
   prm.B = B;

@@ -175,10 +175,8 @@ struct PatView {
   const uint8_t* bflag;
 };
 
-__device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head) {
+__device__ __forceinline__ PatView pattern_of_index(const uint8_t* blob, int pi) {
   const sa_blob_header* hdr = reinterpret_cast<const sa_blob_header*>(blob);
-  const int32_t* head_pat = reinterpret_cast<const int32_t*>(blob + hdr->head_pattern_off);
-  const int pi = head_pat[head];
   const sa_pattern_rec* rec =
       reinterpret_cast<const sa_pattern_rec*>(blob + hdr->pattern_off) + pi;
   PatView v;
@@ -193,6 +191,24 @@ __device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head
   v.row = reinterpret_cast<const int32_t*>(blob + rec->row_off);
   v.bflag = blob + rec->bflag_off;
   return v;
+}
+
+__device__ __forceinline__ PatView pattern_of_head(const uint8_t* blob, int head) {
+  const sa_blob_header* hdr = reinterpret_cast<const sa_blob_header*>(blob);
+  const int32_t* head_pat = reinterpret_cast<const int32_t*>(blob + hdr->head_pattern_off);
+  return pattern_of_index(blob, head_pat[head]);
+}
+
+// The first kArgPatterns patterns travel in the kernel arguments (resolved on
+// the host), so a workgroup reaches its pattern's arrays without a chain of
+// dependent loads through the blob; later patterns are read from the blob.
+constexpr int kArgPatterns = 8;
+struct PatTable {
+  PatView pv[kArgPatterns];
+};
+
+__device__ __forceinline__ PatView pattern_view(const PatTable& t, const uint8_t* blob, int pi) {
+  return pi < kArgPatterns ? t.pv[pi] : pattern_of_index(blob, pi);
 }
 
 // A wave's register window over a tile list (CSR or CSC entries [e0, e1)):
@@ -230,15 +246,16 @@ __device__ __forceinline__ TileWindow tile_window(const int32_t* tile, const uin
 }
 
 // Workgroup -> (batch element, schedule entry) through the per-XCD lists of
-// the layout (workgroup w runs on XCD w % SA_XCDS).  Launch grids are
-// SA_XCDS * len * B workgroups; false = padding, nothing to do.
-__device__ __forceinline__ bool xcd_work_item(const int32_t* xl, int len, int B, int* b,
-                                              int* item) {
+// the layout (workgroup w runs on XCD w % SA_XCDS), whose entries are stored
+// in list order.  Launch grids are SA_XCDS * len * B workgroups; nullptr =
+// padding, nothing to do.
+__device__ __forceinline__ const int32_t* xcd_work_entry(const int32_t* xitems, int len, int B,
+                                                         int* b) {
   const int w = int(blockIdx.x);
   const int x = w % SA_XCDS, j = w / SA_XCDS;
   *b = j / len;
-  *item = xl[x * len + j % len];
-  return *item >= 0 && *b < B;
+  const int32_t* e = xitems + size_t(x * len + j % len) * SA_SCHED_FIELDS;
+  return (*b < B && e[0] >= 0) ? e : nullptr;
 }
 
 }  // namespace sa

@@ -43,8 +43,7 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
 
 struct FwdParams {
   const uint8_t* blob;
-  const int32_t* sched;   // SA_SCHED_FIELDS ints per query-tile entry
-  const int32_t* xl;      // per-XCD lists of schedule entries
+  const int32_t* xitems;  // per-XCD lists of query-tile entries (SA_SCHED_FIELDS ints each)
   int32_t xl_len;
   int32_t B, H, n, num_qslots;
   const void* q;
@@ -57,6 +56,7 @@ struct FwdParams {
   float* part_l;  // [B, num_qslots, BQ]: running sum
   const int32_t* csched;  // (head, q-tile, first slot, chunks) of each split query tile
   float scale_log2;  // softmax scale * log2(e)
+  PatTable pats;     // arrays of the first patterns (device addresses)
 };
 
 // Merge of a split query tile (all chunks have stored their partials): per
@@ -159,11 +159,11 @@ __global__ __launch_bounds__(BQ * 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  int b, item;
-  if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int32_t* it8 = p.sched + SA_SCHED_FIELDS * item;
+  int b;
+  const int32_t* it8 = xcd_work_entry(p.xitems, p.xl_len, p.B, &b);
+  if (!it8) return;
   const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
-  const PatView pv = pattern_of_head(p.blob, head);
+  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const bf16* qg = static_cast<const bf16*>(p.q) + base * kD;
   const bf16* kg = static_cast<const bf16*>(p.k) + base * kD;
@@ -315,11 +315,11 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  int b, item;
-  if (!xcd_work_item(p.xl, p.xl_len, p.B, &b, &item)) return;
-  const int32_t* it8 = p.sched + SA_SCHED_FIELDS * item;
+  int b;
+  const int32_t* it8 = xcd_work_entry(p.xitems, p.xl_len, p.B, &b);
+  if (!it8) return;
   const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
-  const PatView pv = pattern_of_head(p.blob, head);
+  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const float* qg = static_cast<const float*>(p.q) + base * kD;
   const float* kg = static_cast<const float*>(p.k) + base * kD;
@@ -526,8 +526,8 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
 
   FwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
-  prm.sched = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_sched_off);
-  prm.xl = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xl_off);
+  prm.xitems = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xitem_off);
+  fill_pattern_table(blob_host, blob_dev, &prm.pats);
   prm.xl_len = li.fwd_xl_len;
   prm.B = B;
   prm.H = H;

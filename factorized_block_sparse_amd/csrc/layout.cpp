@@ -223,7 +223,7 @@ struct Writer {
 struct SchedItem {
   int32_t head, tile, work;
   int32_t e0 = 0, e1 = 0, slot = -1;
-  int32_t group = -1, slot0 = -1, nchunks = 1;  // split tile: merge group, its slots
+  int32_t pattern = 0, slot0 = -1, nchunks = 1;  // head's pattern; split tile: its slots
 };
 
 // Per-XCD lists over the sorted schedule `sorted` (work in sorted order):
@@ -266,14 +266,14 @@ int32_t xcd_lists(const std::vector<SchedItem>& sorted, std::vector<int32_t>& ou
 }
 
 // Heaviest first; ties keep (head, tile) order.  SA_SCHED_FIELDS ints per
-// entry: (head, tile, e0, e1, slot, group, slot0, nchunks).
+// entry: (head, tile, e0, e1, slot, pattern, slot0, nchunks).
 std::vector<int32_t> sorted_schedule(std::vector<SchedItem>& items) {
   std::stable_sort(items.begin(), items.end(),
                    [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
   std::vector<int32_t> out;
   out.reserve(items.size() * SA_SCHED_FIELDS);
   for (const auto& it : items)
-    out.insert(out.end(), {it.head, it.tile, it.e0, it.e1, it.slot, it.group, it.slot0, it.nchunks});
+    out.insert(out.end(), {it.head, it.tile, it.e0, it.e1, it.slot, it.pattern, it.slot0, it.nchunks});
   return out;
 }
 
@@ -336,7 +336,6 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         continue;
       }
       const int32_t chunks = (len + qcap - 1) / qcap;
-      const int32_t group = int32_t(comb_sched.size() / 4);
       comb_sched.insert(comb_sched.end(), {h, qt, num_qslots, chunks});
       for (int32_t c = 0; c < chunks; ++c) {
         SchedItem it{h, qt, 0};
@@ -344,7 +343,6 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         it.e1 = r0 + int32_t(int64_t(len) * (c + 1) / chunks);
         it.work = it.e1 - it.e0;
         it.slot = num_qslots + c;
-        it.group = group;
         it.slot0 = num_qslots;
         it.nchunks = chunks;
         fwd_items.push_back(it);
@@ -363,7 +361,6 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       }
       // Split into `chunks` nearly equal runs of CSC entries, one partial slot each.
       const int32_t chunks = (len + cap - 1) / cap;
-      const int32_t group = int32_t(red_sched.size() / 4);
       red_sched.insert(red_sched.end(), {h, kt, num_slots, chunks});
       for (int32_t c = 0; c < chunks; ++c) {
         SchedItem it{h, kt, 0};
@@ -371,7 +368,6 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         it.e1 = c0 + int32_t(int64_t(len) * (c + 1) / chunks);
         it.work = it.e1 - it.e0 + 1;
         it.slot = num_slots + c;
-        it.group = group;
         it.slot0 = num_slots;
         it.nchunks = chunks;
         bwd_items.push_back(it);
@@ -379,11 +375,24 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       num_slots += chunks;
     }
   }
+  for (auto& it : fwd_items) it.pattern = head_pat[it.head];
+  for (auto& it : bwd_items) it.pattern = head_pat[it.head];
   const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
   std::vector<int32_t> fwd_xl, bwd_xl;
   const int32_t fwd_xl_len = xcd_lists(fwd_items, fwd_xl);
   const int32_t bwd_xl_len = xcd_lists(bwd_items, bwd_xl);
+  // The entries in list order (padding: all -1).
+  auto list_items = [](const std::vector<int32_t>& xl, const std::vector<int32_t>& sched) {
+    std::vector<int32_t> out;
+    out.reserve(xl.size() * SA_SCHED_FIELDS);
+    for (const int32_t idx : xl)
+      for (int f = 0; f < SA_SCHED_FIELDS; ++f)
+        out.push_back(idx < 0 ? -1 : sched[size_t(idx) * SA_SCHED_FIELDS + f]);
+    return out;
+  };
+  const std::vector<int32_t> fwd_xitem = list_items(fwd_xl, fwd_sched);
+  const std::vector<int32_t> bwd_xitem = list_items(bwd_xl, bwd_sched);
 
   // Two passes: size, then write.
   for (int pass = 0; pass < 2; ++pass) {
@@ -400,6 +409,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.fwd_xl_off = w.put(fwd_xl);
     hdr.comb_sched_off = w.put(comb_sched);
     hdr.bwd_xl_off = w.put(bwd_xl);
+    hdr.fwd_xitem_off = w.put(fwd_xitem);
+    hdr.bwd_xitem_off = w.put(bwd_xitem);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
       sa_pattern_rec& r = recs[i];
@@ -504,7 +515,9 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
       !in_blob(h.bwd_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.bwd_sched_len), total) ||
       !in_blob(h.red_sched_off, 16 * int64_t(h.red_sched_len), total) || h.num_slots < 0 ||
       !in_blob(h.fwd_xl_off, 4 * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
-      !in_blob(h.bwd_xl_off, 4 * int64_t(SA_XCDS) * h.bwd_xl_len, total))
+      !in_blob(h.bwd_xl_off, 4 * int64_t(SA_XCDS) * h.bwd_xl_len, total) ||
+      !in_blob(h.fwd_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
+      !in_blob(h.bwd_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwd_xl_len, total))
     return SA_EINVAL;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

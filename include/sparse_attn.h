@@ -112,7 +112,7 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 6u
+#define SA_BLOB_VERSION 7u
 #define SA_SCHED_FIELDS 8
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
@@ -159,9 +159,9 @@ typedef struct {
   int64_t head_pattern_off; /* int32[num_heads]: pattern index of each head */
   int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
   int64_t fwd_sched_off;    /* int32[SA_SCHED_FIELDS * fwd_sched_len]: (head, q-tile,
-                               first CSR entry, end CSR entry, partial slot, merge group,
-                               first slot of the group, chunks of the group), heaviest
-                               first; unsplit tiles have slot = group = slot0 = -1 and
+                               first CSR entry, end CSR entry, partial slot, pattern index
+                               of the head, first slot of the tile, chunks of the tile),
+                               heaviest first; unsplit tiles have slot = slot0 = -1 and
                                chunks = 1 */
   int64_t bwd_sched_off;    /* int32[SA_SCHED_FIELDS * bwd_sched_len]: the same fields over
                                k-tiles and CSC entries */
@@ -178,6 +178,10 @@ typedef struct {
   int64_t fwd_xl_off;       /* int32[SA_XCDS * fwd_xl_len], indices into fwd_sched */
   int64_t bwd_xl_off;       /* int32[SA_XCDS * bwd_xl_len], indices into bwd_sched */
   int32_t fwd_xl_len, bwd_xl_len;
+  int64_t fwd_xitem_off;    /* int32[SA_XCDS * fwd_xl_len * SA_SCHED_FIELDS]: the entries
+                               the lists name, in list order (all -1 for padding), so a
+                               workgroup finds its work with a single read */
+  int64_t bwd_xitem_off;    /* the same for bwd_sched */
   int64_t comb_sched_off;   /* int32[4 * comb_sched_len]: (head, q-tile, first slot, chunks) */
   int32_t comb_sched_len;
   int32_t num_qslots;       /* query-tile partial slots per batch element */

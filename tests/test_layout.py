@@ -123,12 +123,14 @@ def test_schedules_cover_every_tile_heaviest_first():
     h = lay.header
     fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
     fwork, bwork = [], []
-    for head, qt, e0, e1, slot, group, slot0, nch in fs:
-        assert (group, slot0, nch) == (-1, -1, 1)
+    hp = lay.head_pattern_index()
+    for head, qt, e0, e1, slot, pat, slot0, nch in fs:
+        assert (pat, slot0, nch) == (hp[head], -1, 1)
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
         assert (e0, e1, slot) == (a["row_ptr"][qt], a["row_ptr"][qt + 1], -1)  # no split at n=1000
         fwork.append(e1 - e0)
-    for head, kt, e0, e1, slot, group, slot0, nch in bs:
+    for head, kt, e0, e1, slot, pat, slot0, nch in bs:
+        assert pat == hp[head]
         bwork.append(e1 - e0)
     assert all(w > 0 for w in fwork)
     assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
@@ -150,6 +152,11 @@ def test_xcd_lists_cover_every_schedule_entry_once(n, bq, bk, heads):
     for which, sched in (("fwd", lay.fwd_schedule()), ("bwd", lay.bwd_schedule())):
         xl = lay.xcd_lists(which)
         assert xl.shape[0] == bd.SA_XCDS
+        items = lay.xcd_items(which)  # the named entries, in list order
+        for x in range(bd.SA_XCDS):
+            for j, idx in enumerate(xl[x]):
+                expect = sched[idx] if idx >= 0 else np.full(bd.SA_SCHED_FIELDS, -1)
+                np.testing.assert_array_equal(items[x, j], expect)
         flat = xl[xl >= 0]
         assert sorted(flat.tolist()) == list(range(len(sched)))
         keys = [tuple(int(x) for x in sched[i][:3]) for i in range(len(sched))]
@@ -198,8 +205,7 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
                 s0, nch = red[(head, kt)]
                 assert [r[2] for r in rows] == list(range(s0, s0 + nch))
                 grp = {(int(r[5]), int(r[6]), int(r[7])) for r in bs if r[0] == head and r[1] == kt}
-                gidx = [i for i, r in enumerate(rs) if (r[0], r[1]) == (head, kt)]
-                assert grp == {(gidx[0], s0, nch)}
+                assert grp == {(int(lay.head_pattern_index()[head]), s0, nch)}
     if n == 12288:
         assert h.red_sched_len > 0 and h.num_slots > h.red_sched_len
 
@@ -242,8 +248,7 @@ def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
                 assert nch == -(-(r1 - r0) // qcap)
                 assert [r[2] for r in rows] == list(range(s0, s0 + nch))
                 grp = {(int(r[5]), int(r[6]), int(r[7])) for r in fs if r[0] == head and r[1] == qt}
-                gidx = [i for i, r in enumerate(cs) if (r[0], r[1]) == (head, qt)]
-                assert grp == {(gidx[0], s0, nch)}
+                assert grp == {(int(lay.head_pattern_index()[head]), s0, nch)}
     if n == 12288:
         # summary heads read up to 3072 keys per row; strided heads stay within one class
         assert (h.comb_sched_len > 0) == any(p.kind == "summary" for p in heads)
