@@ -66,7 +66,6 @@ struct BwdParams {
 template <int BQ, int BK>
 __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BQ / 32;
-  constexpr int NT = NW * 64;
   constexpr int NKB = BK / 32;
   constexpr int IPW = BK / 8 / NW;  // 1 KB direct loads per wave, tensor and tile
   static_assert(IPW >= 1 && (BK / 8) % NW == 0, "tile/wave mismatch");
@@ -243,7 +242,6 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 template <int BQ, int BK>
 __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
-  constexpr int NT = NW * 64;
   constexpr int QS = BQ < 64 ? BQ : 64;
   constexpr int NSTEP = BQ / QS;
   constexpr int NQB = QS / 32;

@@ -152,7 +152,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 
 // scheduler room to overlap the next tile's LDS reads and MFMAs with the
 // softmax (measured faster than the 4 waves the kernel could fit).
 template <int BQ, int BK>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ >= 64 ? 3 : 2, BQ >= 64 ? 3 : 2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NKB = BK / 32;
