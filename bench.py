@@ -62,6 +62,26 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
     raise ValueError(label)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "fwd_merge": "fwd_merge_kernel", "bwd_dq": "bwd_dq_kernel",
+                "bwd_dkdv": "bwd_dkdv_kernel", "bwd_merge": "bwd_merge_kernel"}
+
+
+def measured_traffic(label: str, w):
+    """HBM bytes (fetched + written) per launch of this kernel, from the committed
+    counter summary; None when there is none or the kernel sources changed since."""
+    from factorized_block_sparse_amd import profiling
+    recorded, table = profiling.read_traffic(TRAFFIC_FILE)
+    if recorded is None or recorded != profiling.source_hash():
+        return None
+    if label == "fwd_merge":
+        key = f"{KERNEL_NAMES[label]}IDF16bLi{w.block_q}E"
+    else:
+        key = f"{KERNEL_NAMES[label]}<{w.block_q}, {w.block_k}>"
+    hits = [v for name, v in table.items() if key in name]
+    return round(sum(hits[0])) if len(hits) == 1 else None
+
+
 def roofline_entry(flops: float, nbytes: float, seconds: float):
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if flops / max(nbytes, 1) >= ridge:
@@ -263,7 +283,8 @@ def main():
                           "pairs": r["pairs"], "tile_padding_overhead": round(r["padding"], 3)}
     dom = max(kernels, key=lambda k: k["ms"])
     roof = roofline_entry(dom["flops"], dom["bytes"], dom["ms"] * 1e-3)
-    roof.update({"traffic": None, "kernel": f"{dom['kernel']} ({dom['workload']})",
+    roof.update({"traffic": measured_traffic(dom["kernel"], W.WORKLOADS[dom["workload"]]),
+                 "kernel": f"{dom['kernel']} ({dom['workload']})",
                  "launch_us": round(dom["ms"] * 1e3, 2), "event_overhead_us": round(event_us, 2)})
     for k in kernels:
         k["ms"] = round(k["ms"], 4)

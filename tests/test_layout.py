@@ -459,3 +459,18 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert hdr.red_sched_len > 0 and hdr.comb_sched_len > 0
     assert size.value == (rnd(3 * 2 * 12288 * 4) + rnd(3 * hdr.num_slots * 2 * 64 * 64 * 4)
                           + rnd(3 * hdr.num_qslots * 64 * 64 * 4))
+
+
+def test_profile_summaries_parse_and_track_the_sources(tmp_path):
+    """The committed counter summary lists the bench kernels; a summary whose source hash
+    differs from the current kernels is ignored (its traffic would describe other code)."""
+    from factorized_block_sparse_amd import profiling
+    path = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
+    recorded, table = profiling.read_traffic(path)
+    assert recorded is not None and len(recorded) == 64
+    assert any("bwd_dkdv_kernel<128, 64>" in k for k in table)
+    assert all(f > 0 and w > 0 for f, w in table.values())
+    stale = tmp_path / "t.txt"
+    stale.write_text(open(path).read().replace(recorded, "0" * 64))
+    rec2, _ = profiling.read_traffic(str(stale))
+    assert rec2 != profiling.source_hash()
