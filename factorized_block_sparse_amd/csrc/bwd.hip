@@ -118,7 +118,6 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const bf16* kg = p.k + base * kD;
   const bf16* vg = p.v + base * kD;
   const int drow = lane >> 3;
-  const int dcol = ((lane & 7) ^ drow) * 8;
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
@@ -127,6 +126,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   auto dload = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
+      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
       dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
       dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
@@ -296,7 +296,6 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const bf16* qgl = p.q + base * kD;
   const bf16* dgl = p.dout + base * kD;
   const int drow = lane >> 3;
-  const int dcol = ((lane & 7) ^ drow) * 8;
   float lse_r = 0.f, dd_r = 0.f;
   int lo_r = 1, hi_r = 0;
   int qidx[IPW], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
@@ -312,6 +311,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     const int r0 = (ent >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
+      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(qidx[i] < 0 ? 0 : qidx[i]) * kD + dcol;
       dma16(qgl + off, &sq[buf][8 * (w * IPW + i) * kD]);
       dma16(dgl + off, &sdo[buf][8 * (w * IPW + i) * kD]);

@@ -87,17 +87,25 @@ __device__ __forceinline__ bf16x8 load_a_transposed(const bf16* m, int stride, i
 //
 // A tile is row-major [rows][64] bf16 (128 bytes per row, no padding); the
 // eight 16-byte chunks of row r are stored XOR-swizzled, logical chunk c at
-// physical chunk c ^ (r & 7), so that reads of one chunk column over eight
-// consecutive rows hit eight different bank groups.
+// physical chunk c ^ key(r) with key(r) = 2 (r mod 4) + bit 3 of r.  The key
+// serves both read patterns of the kernels without bank conflicts:
+//   16-byte operand reads: each group of 8 lanes reads one chunk column of
+//     rows {0,1,2,3,8,9,10,11} (+4) (the sigma row order): the keys of those
+//     rows are all different;
+//   transposing 8-byte reads: each group of 16 lanes reads chunks c and c^1
+//     of 4 consecutive rows 4a..4a+3: their keys are 2m + const, m = 0..3,
+//     so the 8 (row, chunk) pairs land on 8 different chunk slots.
 //
 // The gfx950 16-byte global->LDS load writes lane L's 16 bytes to
 // lds_base + 16 L (lds_base wave-uniform): one instruction fills a 1 KB block
 // = 8 rows.  Lane L therefore fetches row (L / 8) of its block, logical chunk
-// (L % 8) ^ (L / 8).  The loads count on vmcnt; wait_vmem() before the
+// (L % 8) ^ key(row).  The loads count on vmcnt; wait_vmem() before the
 // barrier that publishes the tile.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz_key(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kD + ((chunk ^ (row & 7)) << 3);
+  return row * kD + ((chunk ^ swz_key(row)) << 3);
 }
 
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {

@@ -191,7 +191,6 @@ void fwd_bf16_kernel(FwdParams p) {
   // tile with its i-th direct load.  Padding keys (map entry -1) fetch token
   // 0 instead: they are never visible, so their probabilities are exactly 0.
   const int drow = lane >> 3;
-  const int dcol = ((lane & 7) ^ drow) * 8;  // element offset of the fetched chunk
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
@@ -200,6 +199,7 @@ void fwd_bf16_kernel(FwdParams p) {
   auto dload = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
+      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
       dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
       dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
