@@ -28,6 +28,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace sa {
@@ -69,8 +71,11 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   constexpr int NKB = BK / 32;
   constexpr int IPW = BK / 8 / NW;  // 1 KB direct loads per wave, tensor and tile
   static_assert(IPW >= 1 && (BK / 8) % NW == 0, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * kD];  // swizzled tiles
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * kD];
+  // Swizzled tiles, two buffers per tensor as separate arrays selected by a
+  // compile-time parity (loop unrolled by two), so that reads of one buffer
+  // are not made to wait for the direct loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) bf16 k0s[BK * kD], k1s[BK * kD];
+  __shared__ __attribute__((aligned(16))) bf16 v0s[BK * kD], v1s[BK * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -123,13 +128,16 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 #pragma unroll
     for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
   };
-  auto dload = [&](int buf) {
+  auto dload = [&](auto par) {
+    constexpr int P = decltype(par)::value;
+    bf16* kd = P ? k1s : k0s;
+    bf16* vd = P ? v1s : v0s;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
-      dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
-      dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
+      dma16(kg + off, kd + 8 * (w * IPW + i) * kD);
+      dma16(vg + off, vd + 8 * (w * IPW + i) * kD);
     }
   };
 
@@ -139,18 +147,21 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
     iload(win.get(e0) >> 1);
-    dload(0);
+    dload(std::integral_constant<int, 0>{});
     if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }
   wait_vmem();
   __syncthreads();
-  for (int it = e0; it < e1; ++it) {
-    const int buf = (it - e0) & 1;
+  // One key tile; P = parity of (it - e0) selects the buffers.
+  auto key_step = [&](auto par, int it) {
+    constexpr int P = decltype(par)::value;
+    const bf16* kcur = P ? k1s : k0s;
+    const bf16* vcur = P ? v1s : v0s;
     const int ent = win.get(it);
     const int kt = ent >> 1;
     const bool full = (ent & 1) != 0;
     if (it + 1 < e1) {
-      dload(buf ^ 1);                                  // tile it+1, indices already here
+      dload(std::integral_constant<int, 1 - P>{});       // tile it+1, indices already here
       if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
@@ -166,8 +177,8 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int off = swz(kr, g + 2 * c);
-          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][off]), qf[c], s);
-          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vs[buf][off]), dof[c], dp);
+          s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&kcur[off]), qf[c], s);
+          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vcur[off]), dof[c], dp);
         }
         // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
         const int lo_rel = lo - k0 - 32 * kb - 8 * g, hi_rel = hi - k0 - 32 * kb - 8 * g;
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
           const bf16x8 db = pack_bf16x8(&ds[8 * h8]);
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
-            dqa[fb] = mfma_bf16(load_a_transposed_swz(ks[buf], 32 * kb + 16 * h8, 32 * fb, lane),
+            dqa[fb] = mfma_bf16(load_a_transposed_swz(kcur, 32 * kb + 16 * h8, 32 * fb, lane),
                                 db, dqa[fb]);
         }
       }
@@ -199,6 +210,10 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     }
     wait_vmem();  // tile it+1 is in LDS (this wave's part)
     __syncthreads();
+  };
+  for (int it = e0; it < e1; it += 2) {
+    key_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < e1) key_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // Register r of half g: feature 32*fb + kappa(r, g); lane = query row.
@@ -248,8 +263,11 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int IPW = QS / 8 / NW;  // 1 KB direct loads per wave, tensor and step
   static_assert(IPW >= 1 && (QS / 8) % NW == 0, "tile/wave mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 sq[2][QS * kD];  // swizzled tiles
-  __shared__ __attribute__((aligned(16))) bf16 sdo[2][QS * kD];
+  // Swizzled tiles, two buffers per tensor as separate arrays selected by a
+  // compile-time parity (loop unrolled by two), so that reads of one buffer
+  // are not made to wait for the direct loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) bf16 q0s[QS * kD], q1s[QS * kD];
+  __shared__ __attribute__((aligned(16))) bf16 o0s[QS * kD], o1s[QS * kD];
   // LSE * log2(e) and -D of each staged query row.  -D seeds the dP
   // accumulator (the MFMA then yields dP - D directly).
   __shared__ __attribute__((aligned(16))) float slse[2][QS];
@@ -306,15 +324,18 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     for (int i = 0; i < IPW; ++i) qidx[i] = pv.qmap[r0 + 8 * (w * IPW + i) + drow];
     if (tid < QS) rtok = pv.qmap[r0 + tid];
   };
-  auto gload = [&](int step, int buf) {
+  auto gload = [&](int step, auto par) {
+    constexpr int P = decltype(par)::value;
+    bf16* qd = P ? q1s : q0s;
+    bf16* od = P ? o1s : o0s;
     const int ent = win.get(c0 + step / NSTEP);
     const int r0 = (ent >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(qidx[i] < 0 ? 0 : qidx[i]) * kD + dcol;
-      dma16(qgl + off, &sq[buf][8 * (w * IPW + i) * kD]);
-      dma16(dgl + off, &sdo[buf][8 * (w * IPW + i) * kD]);
+      dma16(qgl + off, qd + 8 * (w * IPW + i) * kD);
+      dma16(dgl + off, od + 8 * (w * IPW + i) * kD);
     }
     if (tid < QS) {
       const int r = r0 + tid;
@@ -339,19 +360,23 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   if (nsteps > 0) {
     iload(0);
-    gload(0, 0);
+    gload(0, std::integral_constant<int, 0>{});
     if (nsteps > 1) iload(1);
   }
   wait_vmem();
   mstore(0);
   __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
+  // One query step; P = parity of the step selects the buffers.
+  auto q_step = [&](auto par, int step) {
+    constexpr int P = decltype(par)::value;
+    constexpr int buf = P;
+    const bf16* qcur = P ? q1s : q0s;
+    const bf16* ocur = P ? o1s : o0s;
     // PARTIAL tiles set hidden scores to -inf (probability 0) under one
     // uniform branch; FULL tiles (every pair visible) skip it.
     const bool full = (win.get(c0 + step / NSTEP) & 1) != 0;
     if (step + 1 < nsteps) {
-      gload(step + 1, buf ^ 1);               // indices already here
+      gload(step + 1, std::integral_constant<int, 1 - P>{});  // indices already here
       if (step + 2 < nsteps) iload(step + 2);
     }
 #pragma unroll
@@ -369,8 +394,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int off = swz(qr, g + 2 * c);
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sq[buf][off]), kq[c], s);
-        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&sdo[buf][off]), vq[c], dp);
+        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&qcur[off]), kq[c], s);
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ocur[off]), vq[c], dp);
       }
       if (!full) {
 #pragma unroll
@@ -411,14 +436,18 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
           const int q0 = 32 * qb + 16 * h8;
-          dva[fb] = mfma_bf16(load_a_transposed_swz(sdo[buf], q0, 32 * fb, lane), pb, dva[fb]);
-          dka[fb] = mfma_bf16(load_a_transposed_swz(sq[buf], q0, 32 * fb, lane), sb, dka[fb]);
+          dva[fb] = mfma_bf16(load_a_transposed_swz(ocur, q0, 32 * fb, lane), pb, dva[fb]);
+          dka[fb] = mfma_bf16(load_a_transposed_swz(qcur, q0, 32 * fb, lane), sb, dka[fb]);
         }
       }
     }
     wait_vmem();  // step+1 staged (this wave's part)
     if (step + 1 < nsteps) mstore(buf ^ 1);
     __syncthreads();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    q_step(std::integral_constant<int, 0>{}, step);
+    if (step + 1 < nsteps) q_step(std::integral_constant<int, 1>{}, step + 1);
   }
 
   // Register r of half g: feature 32*fb + kappa(r, g); lane = key.

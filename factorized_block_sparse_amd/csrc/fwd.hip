@@ -32,6 +32,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace sa {
@@ -158,8 +160,12 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int NKB = BK / 32;
   constexpr int IPW = BK / 8 / NW;  // 1 KB direct loads per wave, tensor and tile
   static_assert(IPW >= 1 && (BK / 8) % NW == 0, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 ks[2][BK * kD];
-  __shared__ __attribute__((aligned(16))) bf16 vs[2][BK * kD];
+  // Two buffers per tensor as separate arrays, selected by a compile-time
+  // parity (the loop is unrolled by two): the compiler can then tell that the
+  // reads of one buffer never touch the direct loads in flight into the other,
+  // and does not drain those loads before the reads.
+  __shared__ __attribute__((aligned(16))) bf16 k0s[BK * kD], k1s[BK * kD];
+  __shared__ __attribute__((aligned(16))) bf16 v0s[BK * kD], v1s[BK * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -196,13 +202,16 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
   };
-  auto dload = [&](int buf) {
+  auto dload = [&](auto par) {
+    constexpr int P = decltype(par)::value;
+    bf16* kd = P ? k1s : k0s;
+    bf16* vd = P ? v1s : v0s;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
       const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
-      dma16(kg + off, &ks[buf][8 * (w * IPW + i) * kD]);
-      dma16(vg + off, &vs[buf][8 * (w * IPW + i) * kD]);
+      dma16(kg + off, kd + 8 * (w * IPW + i) * kD);
+      dma16(vg + off, vd + 8 * (w * IPW + i) * kD);
     }
   };
 
@@ -215,18 +224,21 @@ void fwd_bf16_kernel(FwdParams p) {
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
     iload(win.get(e0) >> 1);
-    dload(0);
+    dload(std::integral_constant<int, 0>{});
     if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }
   wait_vmem();
   __syncthreads();
-  for (int it = e0; it < e1; ++it) {
-    const int buf = (it - e0) & 1;
+  // One tile; P = parity of (it - e0) selects the buffers.
+  auto tile_step = [&](auto par, int it) {
+    constexpr int P = decltype(par)::value;
+    const bf16* kcur = P ? k1s : k0s;
+    const bf16* vcur = P ? v1s : v0s;
     const int ent = win.get(it);
     const int kt = ent >> 1;
     const bool full = (ent & 1) != 0;
     if (it + 1 < e1) {
-      dload(buf ^ 1);                                  // tile it+1, indices already here
+      dload(std::integral_constant<int, 1 - P>{});       // tile it+1, indices already here
       if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
@@ -239,7 +251,7 @@ void fwd_bf16_kernel(FwdParams p) {
         const int kr = 32 * kb + sigma32(l32);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          s[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ks[buf][swz(kr, g + 2 * c)]), qf[c],
+          s[kb] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&kcur[swz(kr, g + 2 * c)]), qf[c],
                             s[kb]);
       }
       if (!full) {
@@ -290,13 +302,17 @@ void fwd_bf16_kernel(FwdParams p) {
           const bf16x8 pb = pack_bf16x8(tmp);
 #pragma unroll
           for (int fb = 0; fb < 2; ++fb)
-            oacc[fb] = mfma_bf16(load_a_transposed_swz(vs[buf], 32 * kb + 16 * h8, 32 * fb, lane),
+            oacc[fb] = mfma_bf16(load_a_transposed_swz(vcur, 32 * kb + 16 * h8, 32 * fb, lane),
                                  pb, oacc[fb]);
         }
       }
     }
     wait_vmem();  // tile it+1 is in LDS (this wave's part)
     __syncthreads();
+  };
+  for (int it = e0; it < e1; it += 2) {
+    tile_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < e1) tile_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   fwd_epilogue<bf16, BQ>(p, oacc, m_run, pair_sum(l_run), tok, base, b, it8[4], w * 32 + l32, g);
