@@ -80,9 +80,11 @@ WORKLOADS = {
                  note="strided pattern at the CIFAR-10 context length"),
         Workload("fixed_n12288", 2, 8, 12288, 64, fixed_heads(8, 128, 32), "bf16", 128, 64, 1003,
                  note="fixed pattern at the Enwik8 context length, l=128, c=32"),
-        Workload("strided_n12288", 1, 16, 12288, 64, strided_heads(16, 128), "bf16", 64, 64, 1004,
+        Workload("strided_n12288", 1, 16, 12288, 64, strided_heads(16, 128), "bf16", 32, 32, 1004,
                  sinusoid=True,
-                 note="strided pattern at 12,288 with a shared period-128 sinusoid in Q and K"),
+                 note="strided pattern at 12,288 with a shared period-128 sinusoid in Q and K; "
+                      "32x32 tiles (the 96-token residue classes of the stride head fill whole "
+                      "tiles; fastest in a sweep of tile shapes)"),
         Workload("strided_n65536", 1, 8, 65536, 64, strided_heads(8, 256), "bf16", 64, 64, 1005,
                  note="long strided pattern at the audio length 65,536"),
     )
