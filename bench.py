@@ -13,11 +13,17 @@ resident in HBM:
                   shared period-128 sinusoid in Q and K
 Timing: W untimed warm-up steps; then K steps between two HIP events with
 nothing else recorded (ms_per_step, value); then K more steps with an event
-pair around every launch for the per-kernel table and the roofline entry of
-the longest kernel (those intervals include the cost of an event, reported
-as event_overhead_us).
+pair around every launch for the per-kernel table, the forward-only times and
+the roofline entry of the longest kernel (those intervals include the cost of
+an event, reported as event_overhead_us); then K steps with one event between
+consecutive steps (p10 / p50 / p90 of single steps); then K cache-cold steps
+that rotate three input sets; then a vendor bf16 GEMM as a measured peak
+reference.  The layout build is timed once on the host.
 
 Prints one JSON line.  ``--gpus`` above 1 exits: the path runs on one GPU.
+``--sweep-n`` (the O(n sqrt n) scaling check) and ``--crossover`` (dense
+causal against the strided pattern) replace the benchmark with a sweep that
+prints one JSON line per configuration.
 """
 
 from __future__ import annotations
@@ -62,6 +68,16 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
     raise ValueError(label)
 
 
+def algorithmic_bytes(w) -> int:
+    """HBM bytes one forward (+ backward) of a workload must move: the forward
+    reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO and
+    LSE and writes dQ, dK, dV."""
+    elt = 2 if w.dtype == "bf16" else 4
+    rows = w.B * w.H * w.n
+    fwd = rows * (4 * D * elt + 4)
+    return fwd + (rows * (8 * D * elt + 4) if w.backward else 0)
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "fwd_merge": "fwd_merge_kernel", "bwd_dq": "bwd_dq_kernel",
                 "bwd_dkdv": "bwd_dkdv_kernel", "bwd_merge": "bwd_merge_kernel"}
@@ -82,6 +98,62 @@ def measured_traffic(label: str, w):
     return round(sum(hits[0])) if len(hits) == 1 else None
 
 
+def cache_cold_step_ms(torch, bd, runs, K: int) -> float:
+    """ms per fwd+bwd step when each step uses another of three input sets."""
+    sets = []
+    for r in runs:
+        q, k, v, do, o, lse, grads, ws, fws, dt = r["tensors"]
+        sets.append([(q, k, v, do)] + [tuple(x.clone() for x in (q, k, v, do)) for _ in range(2)])
+
+    def step(j):
+        for r, st in zip(runs, sets):
+            w, lay = r["w"], r["lay"]
+            q, k, v, do = st[j % 3]
+            _, _, _, _, o, lse, grads, ws, fws, dt = r["tensors"]
+            bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws)
+            if w.backward:
+                bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads)
+
+    for j in range(3):
+        step(j)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for j in range(K):
+        step(j)
+    b.record()
+    torch.cuda.synchronize()
+    del sets
+    return a.elapsed_time(b) / K
+
+
+def vendor_gemm_reference(torch):
+    """A measured bf16 MFMA reference on this GPU: torch.matmul (the vendor GEMM
+    library) of two 8192 x 8192 bf16 matrices, best of 3 timings of 10 calls."""
+    try:
+        n = 8192
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 10
+            best = t if best is None else min(best, t)
+        del a, b, c
+        return {"tflops": round(2 * n ** 3 / (best * 1e-3) / 1e12, 1),
+                "what": "torch.matmul bf16 8192x8192x8192, best of 3 x 10 calls"}
+    except Exception:  # reference only; never fails the bench
+        return None
+
+
 def roofline_entry(flops: float, nbytes: float, seconds: float):
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if flops / max(nbytes, 1) >= ridge:
@@ -98,6 +170,16 @@ def roofline_entry(flops: float, nbytes: float, seconds: float):
 # ----------------------------------------------------------------------------
 
 _CPU = {}
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cpu_task(args):
@@ -145,11 +227,126 @@ def cpu_baseline(workloads, inputs, seconds: float):
             flops += f
     wall = time.time() - t0
     return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "host_cpu": host_cpu_model(), "nproc": os.cpu_count(),
             "sample": (f"{rows_done} of the {total_rows} query rows of {'+'.join(w.name for w in workloads)} "
                        f"(random order over every batch element and head) through the float64 row-gather "
                        f"oracle forward+backward in {wall:.1f} s of wall time (deadline {seconds:.0f} s); "
                        f"useful FLOPs 12*d*keys per row"),
             "seconds": wall}
+
+
+# ----------------------------------------------------------------------------
+# sweeps (separate modes; each prints one JSON line per configuration and a
+# summary line)
+# ----------------------------------------------------------------------------
+
+def time_config(torch, bd, W, n: int, heads, block_q: int, block_k: int, B: int, seed: int,
+                steps: int, warmup: int) -> dict:
+    """Forward and forward+backward ms of one layout on seeded bf16 inputs."""
+    H = len(heads)
+    t0 = time.perf_counter()
+    lay = bd.Layout(n, heads, block_q, block_k)
+    layout_ms = 1000 * (time.perf_counter() - t0)
+    inp = W.make_inputs(B, H, n, D, seed)
+    q, k, v, do = (inp[x].to("cuda") for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    fws = torch.empty(max(1, bd.fwd_workspace_bytes(lay, B, H)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(bd.bwd_workspace_bytes(lay, B, H), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws)
+
+    def both():
+        fwd()
+        bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    fwd_ms, both_ms = timed(fwd), timed(both)
+    pairs = lay.pairs_per_batch() * B
+    area = lay.tiles_per_batch() * B * block_q * block_k
+    useful = 12 * D * pairs
+    return {"n": n, "B": B, "H": H, "tiles": [block_q, block_k], "pairs": pairs,
+            "computed_tile_area": area, "tile_padding_overhead": round(area / pairs, 3),
+            "fwd_ms": round(fwd_ms, 4), "fwd_bwd_ms": round(both_ms, 4),
+            "useful_tflops": round(useful / (both_ms * 1e-3) / 1e12, 2),
+            "layout_build_ms": round(layout_ms, 2)}
+
+
+def fit_exponent(xs, ys) -> float:
+    """Least-squares slope of log y against log x."""
+    lx = [math.log(x) for x in xs]
+    ly = [math.log(y) for y in ys]
+    mx, my = sum(lx) / len(lx), sum(ly) / len(ly)
+    return sum((a - mx) * (b - my) for a, b in zip(lx, ly)) / sum((a - mx) ** 2 for a in lx)
+
+
+def sweep_n(args) -> None:
+    """O(n sqrt n) check: strided heads with l = 2^round(log2 sqrt n), 64 x 64
+    tiles, n = 1,024 ... 65,536; fits the growth exponents of allowed pairs,
+    computed-tile area and time."""
+    import torch
+    from factorized_block_sparse_amd import binding as bd
+    from factorized_block_sparse_amd import workloads as W
+    rows = []
+    for e in range(10, 17):
+        n = 1 << e
+        l = 1 << round(math.log2(math.sqrt(n)))
+        r = time_config(torch, bd, W, n, W.strided_heads(8, l), 64, 64, 1, 2000 + e,
+                        args.steps, args.warmup)
+        r.update(mode="sweep_n", l=l, dense_causal_pairs=8 * n * (n + 1) // 2)
+        r["computed_over_dense_causal"] = round(r["computed_tile_area"] / r["dense_causal_pairs"], 4)
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+    ns = [r["n"] for r in rows]
+    big = [r for r in rows if r["n"] >= 8192]
+    print(json.dumps({
+        "mode": "sweep_n_fit", "pattern": "strided, H=8 alternating local/stride, l=2^round(log2 sqrt n)",
+        "exponent_pairs": round(fit_exponent(ns, [r["pairs"] for r in rows]), 3),
+        "exponent_computed_tile_flops": round(fit_exponent(ns, [r["computed_tile_area"] for r in rows]), 3),
+        "exponent_fwd_bwd_time": round(fit_exponent(ns, [r["fwd_bwd_ms"] for r in rows]), 3),
+        "exponent_fwd_bwd_time_n_ge_8192": round(fit_exponent([r["n"] for r in big],
+                                                              [r["fwd_bwd_ms"] for r in big]), 3),
+        "expected": 1.5}), flush=True)
+
+
+def crossover(args) -> None:
+    """Dense causal attention (a local band as wide as the sequence) against the
+    strided pattern (l = 2^round(log2 sqrt n)) in the same kernels, at the same
+    number of tokens per call (B = max(1, 16384 / n), H = 8)."""
+    import torch
+    from factorized_block_sparse_amd import binding as bd
+    from factorized_block_sparse_amd import workloads as W
+    out = []
+    for n in (512, 1024, 2048, 4096, 8192, 16384):
+        B = max(1, 16384 // n)
+        l = 1 << round(math.log2(math.sqrt(n)))
+        dense = time_config(torch, bd, W, n, tuple(W.HeadSpec(W.LOCAL, n) for _ in range(8)), 128, 64,
+                            B, 3000 + n, args.steps, args.warmup)
+        sparse = min((time_config(torch, bd, W, n, W.strided_heads(8, l), t, t, B, 3000 + n,
+                                  args.steps, args.warmup) for t in (32, 64)),
+                     key=lambda r: r["fwd_bwd_ms"])
+        r = {"mode": "crossover", "n": n, "B": B, "l": l, "dense": dense, "sparse": sparse,
+             "fwd_bwd_speedup": round(dense["fwd_bwd_ms"] / sparse["fwd_bwd_ms"], 3),
+             "fwd_speedup": round(dense["fwd_ms"] / sparse["fwd_ms"], 3)}
+        print(json.dumps(r), flush=True)
+        out.append(r)
+    slower = [r["n"] for r in out if r["fwd_bwd_speedup"] < 1.0]
+    print(json.dumps({"mode": "crossover_summary",
+                      "n_where_dense_is_faster": slower,
+                      "speedups": {r["n"]: r["fwd_bwd_speedup"] for r in out}}), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -167,12 +364,20 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the workloads, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, for scaling HBM byte counters)")
+    ap.add_argument("--sweep-n", action="store_true",
+                    help="instead of the benchmark: the O(n sqrt n) sweep, one JSON line per n")
+    ap.add_argument("--crossover", action="store_true",
+                    help="instead of the benchmark: dense causal vs strided, one JSON line per n")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(the attention path is single-GPU; see the design notes for how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep_n or args.crossover:
+        (sweep_n if args.sweep_n else crossover)(args)
+        return
 
     import torch
     from factorized_block_sparse_amd import binding as bd
@@ -190,8 +395,11 @@ def main():
     names = [s for s in args.workloads.split(",") if s]
     wls = [W.WORKLOADS[nm] for nm in names]
     inputs, runs = {}, []
+    layout_ms = {}
     for w in wls:
+        t_lay = time.perf_counter()
         lay = bd.Layout(w.n, w.heads, w.block_q, w.block_k)
+        layout_ms[w.name] = round(1000 * (time.perf_counter() - t_lay), 2)
         inp = W.workload_inputs(w)
         inputs[w.name] = inp
         q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
@@ -220,7 +428,8 @@ def main():
         useful = (12 if w.backward else 4) * D * pairs
         tiles = lay.tiles_per_batch() * w.B
         runs.append(dict(w=w, lay=lay, calls=calls, pairs=pairs, useful=useful,
-                         padding=tiles * w.block_q * w.block_k / pairs))
+                         padding=tiles * w.block_q * w.block_k / pairs,
+                         tensors=(q, k, v, do, o, lse, grads, ws, fws, dt)))
 
     flat = [(r["w"], label, fn) for r in runs for (label, fn) in r["calls"]]
 
@@ -263,6 +472,22 @@ def main():
     per_call_ms = [sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(K)) / K for i in range(len(flat))]
     event_us = 1000 * b2b[0].elapsed_time(b2b[-1]) / (len(b2b) - 1)
 
+    # Step-time distribution: one event between consecutive steps (each
+    # interval includes one event's cost).
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    sev[0].record()
+    for s in range(K):
+        step()
+        sev[s + 1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(sev[s].elapsed_time(sev[s + 1]) for s in range(K))
+    pct = lambda f: step_ms[min(K - 1, int(round(f * (K - 1))))]
+
+    # Cache-cold variant: rotate three input sets (more than the 256 MB
+    # Infinity Cache in total) so that a step does not find its inputs cached.
+    cold_ms = cache_cold_step_ms(torch, bd, runs, K)
+    gemm = vendor_gemm_reference(torch)
+
     useful = sum(r["useful"] for r in runs)
     value = useful / (ms_per_step * 1e-3) / 1e12
 
@@ -278,9 +503,15 @@ def main():
             kernels.append(dict(workload=w.name, kernel=label, ms=t, flops=fl, bytes=by))
             idx += 1
         tf = r["useful"] / (ms * 1e-3) / 1e12
-        per_wl[w.name] = {"ms": round(ms, 4), "useful_tflops": round(tf, 2),
+        alg_bytes = algorithmic_bytes(w)
+        fwd_ms = sum(k["ms"] for k in kernels[-len(r["calls"]):] if k["kernel"].startswith("fwd"))
+        per_wl[w.name] = {"ms": round(ms, 4), "fwd_ms": round(fwd_ms, 4),
+                          "useful_tflops": round(tf, 2),
                           "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-                          "pairs": r["pairs"], "tile_padding_overhead": round(r["padding"], 3)}
+                          "alg_hbm_bytes": alg_bytes,
+                          "pct_hbm_roofline": round(100 * alg_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 2),
+                          "pairs": r["pairs"], "tile_padding_overhead": round(r["padding"], 3),
+                          "layout_build_ms": layout_ms[w.name]}
     dom = max(kernels, key=lambda k: k["ms"])
     roof = roofline_entry(dom["flops"], dom["bytes"], dom["ms"] * 1e-3)
     roof.update({"traffic": measured_traffic(dom["kernel"], W.WORKLOADS[dom["workload"]]),
@@ -307,6 +538,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "pct_of_measured_gemm": round(100 * value / gemm["tflops"], 3) if gemm else None,
+        "measured_gemm_reference": gemm,
+        "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+        "ms_per_step_cache_cold": round(cold_ms, 4),
         "config": {"workload": "+".join(names),
                    "shapes": {w.name: {"B": w.B, "H": w.H, "n": w.n, "d": w.d,
                                        "heads": sorted({h.kind for h in w.heads}),
