@@ -11,11 +11,16 @@ Two kinds of summary, both short text files:
   The file records a hash of the kernel sources, so that a reader can tell
   whether the kernels changed after the counters were taken.
 
+* shader counters: one ``--pmc`` run of SQ counters (MFMA busy cycles, LDS
+  bank conflicts, wait cycles), averaged per dispatch, with the ratios
+  derived from them.
+
 Usage (on the csv files a profiling run wrote):
 
     python -m factorized_block_sparse_amd.profiling stats <kernel_stats.csv> <out.txt> "<command>"
     python -m factorized_block_sparse_amd.profiling traffic <fetch.csv> <write.csv> <copy MiB> \\
         <out.txt> "<fetch command>" "<write command>"
+    python -m factorized_block_sparse_amd.profiling counters <counters.csv> <out.txt> "<command>"
 """
 
 from __future__ import annotations
@@ -69,21 +74,29 @@ def _per_kernel(path: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
 
 
+def _first_copy(path: str) -> float:
+    """Counter value of the first dispatch of the copy kernel: the calibration
+    copy, which runs before anything else copies (later copies, of other sizes,
+    use the same kernel)."""
+    hits = [(int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+            if COPY_KERNEL_MARK in r["Kernel_Name"]]
+    if not hits:
+        raise SystemExit("no copy kernel in the counter files: run with --copy-calibration-mib")
+    return min(hits)[1]
+
+
 def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, dst: str, fetch_cmd: str,
                   write_cmd: str) -> str:
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
-    copy = [k for k in fetch if COPY_KERNEL_MARK in k]
-    if not copy or not any(COPY_KERNEL_MARK in k for k in write):
-        raise SystemExit("no copy kernel in the counter files: run with --copy-calibration-mib")
+    copy_f, copy_w = _first_copy(fetch_csv), _first_copy(write_csv)
     known_kib = copy_mib * 1024.0
-    f_scale = known_kib / fetch[copy[0]][0]
-    w_scale = known_kib / write[[k for k in write if COPY_KERNEL_MARK in k][0]][0]
+    f_scale = known_kib / copy_f
+    w_scale = known_kib / copy_w
     lines = ["# HBM traffic per dispatch from rocprofv3 counters (one MI355X)",
              f"# FETCH_SIZE command: {fetch_cmd}",
              f"# WRITE_SIZE command: {write_cmd}",
-             f"# calibration: a {copy_mib} MiB device-to-device copy counts "
-             f"{fetch[copy[0]][0]:.1f} KiB fetched and "
-             f"{write[[k for k in write if COPY_KERNEL_MARK in k][0]][0]:.1f} KiB written;",
+             f"# calibration: the first dispatch of the copy kernel (a {copy_mib} MiB device-to-device "
+             f"copy) counts {copy_f:.1f} KiB fetched and {copy_w:.1f} KiB written;",
              f"#   scale factors fetch x{f_scale:.4f}, write x{w_scale:.4f} (known / counted)",
              f"# kernel sources sha256: {source_hash()}",
              "# kernel | dispatches | fetch_MB | write_MB  (scaled, per dispatch, 1 MB = 1e6 B)"]
@@ -93,6 +106,55 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, dst: str, fetch
         fb = fetch[k][0] * f_scale * 1024
         wb = write[k][0] * w_scale * 1024
         lines.append(f"{k} | {fetch[k][1]} | {fb / 1e6:.3f} | {wb / 1e6:.3f}")
+    text = "\n".join(lines) + "\n"
+    with open(dst, "w") as f:
+        f.write(text)
+    return text
+
+
+SIMDS_PER_XCD = 128  # 32 CUs x 4 SIMDs in each of the 8 XCDs
+
+
+def _per_kernel_counters(path: str) -> dict:
+    vals = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: (sum(v) / len(v), len(v)) for c, v in d.items()} for k, d in vals.items()}
+
+
+def write_counters(src: str, dst: str, command: str) -> str:
+    """Per-dispatch averages of SQ counters and three ratios:
+    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (128 x GRBM_GUI_ACTIVE), the share
+    of SIMD cycles the matrix units were busy.  GRBM_GUI_ACTIVE reads about 8x
+    the dispatch's duration in shader cycles here (one count per XCD), so
+    128 x GRBM_GUI_ACTIVE is the SIMD-cycles of all 1,024 SIMDs; a 32x32x16
+    bf16 MFMA adds 32 busy cycles (SQ_VALU_MFMA_BUSY_CYCLES = 32 x SQ_INSTS_MFMA
+    in these files).
+    lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS, bank-conflict cycles
+    per LDS instruction.
+    wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, the share of wave lifetime spent
+    waiting on a dependency (s_waitcnt)."""
+    table = _per_kernel_counters(src)
+    names = sorted({c for d in table.values() for c in d})
+    lines = ["# rocprofv3 shader counters per dispatch (one MI355X)",
+             f"# command: {command}",
+             f"# kernel sources sha256: {source_hash()}",
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (128 SIMDs per XCD x GRBM_GUI_ACTIVE, "
+             "which counts once per XCD); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; "
+             "wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES",
+             "# kernel | dispatches | mfma_busy | lds_conflict | wait | " + " | ".join(names)]
+    for k in sorted(table):
+        if "sa::" not in k and "_ZN2sa" not in k:
+            continue
+        d = table[k]
+        g = lambda c: d[c][0] if c in d else float("nan")
+        div = lambda a, b: a / b if b else float("nan")
+        busy = div(g("SQ_VALU_MFMA_BUSY_CYCLES"), SIMDS_PER_XCD * g("GRBM_GUI_ACTIVE"))
+        conf = div(g("SQ_LDS_BANK_CONFLICT"), g("SQ_INSTS_LDS"))
+        wait = div(g("SQ_WAIT_ANY"), g("SQ_WAVE_CYCLES"))
+        n = max(v[1] for v in d.values())
+        lines.append(f"{k} | {n} | {busy:.3f} | {conf:.3f} | {wait:.3f} | "
+                     + " | ".join(f"{g(c):.4g}" for c in names))
     text = "\n".join(lines) + "\n"
     with open(dst, "w") as f:
         f.write(text)
@@ -116,6 +178,8 @@ def read_traffic(path: str) -> tuple[str | None, dict]:
 def main(argv: list[str]) -> None:
     if len(argv) >= 4 and argv[0] == "stats":
         print(write_kernel_stats(argv[1], argv[2], argv[3]))
+    elif len(argv) >= 4 and argv[0] == "counters":
+        print(write_counters(argv[1], argv[2], argv[3]))
     elif len(argv) >= 7 and argv[0] == "traffic":
         print(write_traffic(argv[1], argv[2], int(argv[3]), argv[4], argv[5], argv[6]))
     else:
