@@ -349,6 +349,57 @@ def crossover(args) -> None:
                       "speedups": {r["n"]: r["fwd_bwd_speedup"] for r in out}}), flush=True)
 
 
+def natural_order_tile_area(n: int, head, bq: int, bk: int) -> int:
+    """Computed tile area of one summary or same-block head if its keys kept
+    token order (no packing): a tile pair is computed when it holds a visible
+    pair.  Host arithmetic on the head's definition, for the packing report."""
+    nqt, nkt = -(-n // bq), -(-n // bk)
+    l = head.l
+    area = 0
+    if head.kind == "sameblock":
+        for qt in range(nqt):
+            r0, r1 = qt * bq, min(n, (qt + 1) * bq) - 1
+            lo = (r0 // l) * l
+            area += (r1 // bk - lo // bk + 1) * bq * bk
+        return area
+    c = head.c
+    s = l - ((head.sub % (l // c)) + 1) * c
+    first = []  # first summary cell in each key tile (or None)
+    for kt in range(nkt):
+        j0, j1 = kt * bk, min(n, (kt + 1) * bk) - 1
+        hit = None
+        for base in range((j0 // l) * l, j1 + 1, l):
+            a = max(j0, base + s)
+            if a <= min(j1, base + s + c - 1):
+                hit = a
+                break
+        first.append(hit)
+    for qt in range(nqt):
+        r0, r1 = qt * bq, min(n, (qt + 1) * bq) - 1
+        tiles = {kt for kt in range(nkt) if first[kt] is not None and first[kt] <= r1}
+        tiles |= {i // bk for i in range(r0, min(r1 + 1, s))}  # rows before the first cell read themselves
+        area += len(tiles) * bq * bk
+    return area
+
+
+def summary_width(args) -> None:
+    """Small-c summary packing: the fixed pattern at n = 12,288, l = 128,
+    c = 8, 16, 32 (B = 2, H = 8 alternating same-block / summary), with the
+    tile area that token order would compute beside the packed layout's."""
+    import torch
+    from factorized_block_sparse_amd import binding as bd
+    from factorized_block_sparse_amd import workloads as W
+    n, l = 12288, 128
+    for c in (8, 16, 32):
+        heads = W.fixed_heads(8, l, c)
+        for bq, bk in ((128, 64), (64, 64)):
+            r = time_config(torch, bd, W, n, heads, bq, bk, 2, 4000 + c, args.steps, args.warmup)
+            natural = 2 * sum(natural_order_tile_area(n, h, bq, bk) for h in heads)
+            r.update(mode="summary_width", l=l, c=c,
+                     natural_order_tile_padding_overhead=round(natural / r["pairs"], 3))
+            print(json.dumps(r), flush=True)
+
+
 # ----------------------------------------------------------------------------
 # GPU run
 # ----------------------------------------------------------------------------
@@ -368,6 +419,9 @@ def main():
                     help="instead of the benchmark: the O(n sqrt n) sweep, one JSON line per n")
     ap.add_argument("--crossover", action="store_true",
                     help="instead of the benchmark: dense causal vs strided, one JSON line per n")
+    ap.add_argument("--summary-width", action="store_true",
+                    help="instead of the benchmark: the fixed pattern at c = 8, 16, 32 with packed "
+                         "summary tiles, one JSON line per (c, tiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -375,8 +429,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.sweep_n or args.crossover:
-        (sweep_n if args.sweep_n else crossover)(args)
+    if args.sweep_n or args.crossover or args.summary_width:
+        (sweep_n if args.sweep_n else crossover if args.crossover else summary_width)(args)
         return
 
     import torch

@@ -85,6 +85,9 @@ WORKLOADS = {
                  note="strided pattern at 12,288 with a shared period-128 sinusoid in Q and K; "
                       "32x32 tiles (the 96-token residue classes of the stride head fill whole "
                       "tiles; fastest in a sweep of tile shapes)"),
+        Workload("fixed_c8_n12288", 2, 8, 12288, 64, fixed_heads(8, 128, 8), "bf16", 128, 64, 1006,
+                 note="fixed pattern with narrow summaries (l=128, c=8, the report's own example); "
+                      "the summary cells of consecutive blocks are packed into dense key tiles"),
         Workload("strided_n65536", 1, 8, 65536, 64, strided_heads(8, 256), "bf16", 64, 64, 1005,
                  note="long strided pattern at the audio length 65,536"),
     )

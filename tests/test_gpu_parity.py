@@ -189,7 +189,7 @@ def _sample_rows(n, l, rng, extra=6):
     return sorted(r for r in base if 0 <= r < n)
 
 
-@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "strided_n65536"])
+@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "fixed_c8_n12288", "strided_n65536"])
 def test_workload_full_size_sampled(wname):
     w = W.WORKLOADS[wname]
     lay = Layout(w.n, w.heads, w.block_q, w.block_k)
