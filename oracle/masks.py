@@ -34,6 +34,18 @@ reason, in the design notes of the repository):
 The local + global-token pattern of the same blog post (sections 04, 07 and
 09) is here as well, because its 8-token worked example pins the causal
 local band.
+
+Two further head kinds combine sets in one head:
+
+* ``fixed_merged``: one head reads the union of the two fixed-pattern sets,
+  A_i = same-block_i | summary_i (the merged integration of report section
+  3.1, Eq. 7, which the Enwik8 model used; report section 4).  No row is
+  empty (every row reads itself through its own block).
+* ``local_global``: the causal window of width l plus the first c positions
+  as global tokens (blog post sections 03 and 04): A_i = {j <= i : i - j <= l
+  or j < c}.  A global query (i < c) reads every j <= i, as section 04 asks.
+  Reading: the head kind puts the global tokens at the front; the dense
+  ``local_global_mask`` keeps arbitrary global positions.
 """
 
 from __future__ import annotations
@@ -44,7 +56,9 @@ LOCAL = "local"
 STRIDE = "stride"
 SAMEBLOCK = "sameblock"
 SUMMARY = "summary"
-KINDS = (LOCAL, STRIDE, SAMEBLOCK, SUMMARY)
+FIXED_MERGED = "fixed_merged"
+LOCAL_GLOBAL = "local_global"
+KINDS = (LOCAL, STRIDE, SAMEBLOCK, SUMMARY, FIXED_MERGED, LOCAL_GLOBAL)
 
 
 def summary_start(l: int, c: int, sub: int = 0) -> int:
@@ -84,6 +98,12 @@ def visible(kind: str, i, j, l: int, c: int | None = None, sub: int = 0):
         s = summary_start(l, c, sub)
         r = np.mod(j, l)
         return causal & (r >= s) & (r <= s + c - 1)
+    if kind == FIXED_MERGED:
+        return visible(SAMEBLOCK, i, j, l) | visible(SUMMARY, i, j, l, c, sub)
+    if kind == LOCAL_GLOBAL:
+        if c is None or c < 0:
+            raise ValueError("need a number of global tokens c >= 0")
+        return causal & ((i - j <= l) | (j < c))
     raise ValueError(f"unknown head kind {kind!r}")
 
 
@@ -126,6 +146,14 @@ def row_keys(kind: str, i: int, n: int, l: int, c: int | None = None,
         blocks = np.arange(i // l + 1, dtype=np.int64)
         keys = (blocks[:, None] * l + s + np.arange(c, dtype=np.int64)[None, :]).ravel()
         keys = keys[keys <= i]
+    elif kind == FIXED_MERGED:
+        keys = np.union1d(row_keys(SAMEBLOCK, i, n, l),
+                          row_keys(SUMMARY, i, n, l, c, sub, self_if_empty=False))
+    elif kind == LOCAL_GLOBAL:
+        if c is None or c < 0:
+            raise ValueError("need a number of global tokens c >= 0")
+        keys = np.union1d(np.arange(0, min(c, i + 1), dtype=np.int64),
+                          np.arange(max(0, i - l), i + 1, dtype=np.int64))
     else:
         raise ValueError(f"unknown head kind {kind!r}")
     if keys.size == 0 and self_if_empty:

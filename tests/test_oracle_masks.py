@@ -20,6 +20,10 @@ KINDS_SMALL = [
     (M.SUMMARY, dict(l=8, c=2, sub=0)), (M.SUMMARY, dict(l=8, c=2, sub=1)),
     (M.SUMMARY, dict(l=8, c=2, sub=3)), (M.SUMMARY, dict(l=8, c=3, sub=0)),
     (M.SUMMARY, dict(l=8, c=8, sub=0)), (M.SUMMARY, dict(l=6, c=1, sub=2)),
+    (M.FIXED_MERGED, dict(l=8, c=2, sub=0)), (M.FIXED_MERGED, dict(l=8, c=2, sub=3)),
+    (M.FIXED_MERGED, dict(l=6, c=1, sub=2)), (M.FIXED_MERGED, dict(l=5, c=5, sub=0)),
+    (M.LOCAL_GLOBAL, dict(l=2, c=1)), (M.LOCAL_GLOBAL, dict(l=3, c=0)),
+    (M.LOCAL_GLOBAL, dict(l=4, c=7)), (M.LOCAL_GLOBAL, dict(l=1, c=30)),
 ]
 
 
@@ -111,6 +115,46 @@ def test_summary_printed_example(golden_dir):
     assert not mask[:, 128:248].any()
 
 
+def test_fixed_merged_worked_example(golden_dir):
+    """Report sections 2.2 and 3.1 (Eq. 7): a hand-worked 8-token merged fixed head."""
+    meta, expect = _read_golden_matrix(os.path.join(golden_dir, "fixed_merged_n8_l4_c1.txt"))
+    n, l, c = meta["length"], meta["l"], meta["c"]
+    got = M.head_mask(n, M.FIXED_MERGED, l, c, 0)
+    np.testing.assert_array_equal(got, expect)
+    for i in range(n):
+        assert M.row_keys(M.FIXED_MERGED, i, n, l, c, 0).tolist() == np.flatnonzero(expect[i]).tolist()
+    assert got.sum() == 24
+
+
+def test_fixed_merged_totals_and_special_cases():
+    """Closed-form totals of the merged fixed head; c = l reads every j <= i."""
+    n, l, c = 12288, 128, 32
+    mb = n // l
+    total = mb * l * (l + 1) // 2 + c * l * mb * (mb - 1) // 2
+    assert total == 19470336
+    for sub in (0, 3):
+        got = sum(M.row_keys(M.FIXED_MERGED, i, n, l, c, sub).size for i in range(n))
+        assert got == total
+    # With c = l every position is a summary cell: dense causal.
+    m = M.head_mask(40, M.FIXED_MERGED, 8, 8, 0)
+    np.testing.assert_array_equal(m, np.tril(np.ones((40, 40), dtype=bool)))
+
+
+def test_local_global_kind_is_the_worked_example(golden_dir):
+    """Blog post section 04: window 2 plus global token 0 as the head kind (c = 1 leading token)."""
+    meta, expect = _read_golden_matrix(os.path.join(golden_dir, "local_global_8x8.txt"))
+    assert meta["global"] == 0
+    got = M.head_mask(meta["length"], M.LOCAL_GLOBAL, meta["window"], 1)
+    np.testing.assert_array_equal(got, expect)
+    # Several leading global tokens agree with the dense form of arbitrary global positions.
+    np.testing.assert_array_equal(M.head_mask(50, M.LOCAL_GLOBAL, 4, 6),
+                                  M.local_global_mask(50, 4, tuple(range(6))))
+    # No global tokens: the local head of the strided pattern.
+    np.testing.assert_array_equal(M.head_mask(30, M.LOCAL_GLOBAL, 3, 0), M.head_mask(30, M.LOCAL, 3))
+    with pytest.raises(ValueError):
+        M.head_mask(10, M.LOCAL_GLOBAL, 3, -1)
+
+
 def test_summary_start_of_sub_blocks():
     """Report section 2.2: several summary heads take different c-sized sub-blocks of the l-block."""
     assert [M.summary_start(128, 32, k) for k in range(5)] == [96, 64, 32, 0, 96]
@@ -129,6 +173,13 @@ def _closed_form_count(kind, i, l, c=None, s=None):
         return i // l + 1
     if kind == M.SAMEBLOCK:
         return i % l + 1
+    if kind == M.FIXED_MERGED:
+        # own block up to i, plus c cells of every earlier block (the cells of
+        # the own block up to i are already in it)
+        return i % l + 1 + (i // l) * c
+    if kind == M.LOCAL_GLOBAL:
+        lo = max(0, i - l)
+        return i - lo + 1 + min(c, lo)  # window, plus global tokens before it
     cnt = (i // l) * c + min(max(i % l - s + 1, 0), c)
     return cnt if cnt > 0 else 1
 
