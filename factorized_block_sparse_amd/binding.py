@@ -20,7 +20,8 @@ LIB_NAME = "libsparse_attn.so"
 
 # enum values of sparse_attn.h
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ESIZE, SA_EHIP = 0, -1, -2, -3, -4
-KINDS = {"local": 0, "stride": 1, "sameblock": 2, "summary": 3}
+KINDS = {"local": 0, "stride": 1, "sameblock": 2, "summary": 3, "fixed_merged": 4,
+         "local_global": 5}
 SA_BF16, SA_FP32 = 0, 1
 SA_SELF_IF_EMPTY = 1
 SA_BLOB_MAGIC = 0x31415053
@@ -53,7 +54,7 @@ class CPatternRec(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("l", ctypes.c_int32), ("c", ctypes.c_int32),
                 ("sub", ctypes.c_int32), ("s", ctypes.c_int32), ("nnz", ctypes.c_int32),
                 ("pairs", ctypes.c_int64)] + [
-        (f, ctypes.c_int64) for f in ("qmap_off", "kmap_off", "lo_off", "hi_off", "count_off",
+        (f, ctypes.c_int64) for f in ("qmap_off", "kmap_off", "lo_off", "hi_off", "pre_off", "count_off",
                                       "row_ptr_off", "col_off", "fflag_off", "col_ptr_off",
                                       "row_off", "bflag_off")]
 
@@ -143,7 +144,9 @@ def _check(rc: int, what: str):
 
 @dataclass(frozen=True)
 class HeadPattern:
-    """One head's pattern: kind in {"local", "stride", "sameblock", "summary"}."""
+    """One head's pattern: kind in {"local", "stride", "sameblock", "summary",
+    "fixed_merged", "local_global"}; c is the summary width, or for
+    "local_global" the number of leading global tokens."""
     kind: str
     l: int
     c: int = 0
@@ -210,6 +213,8 @@ class Layout:
             "kmap": self._arr(r.kmap_off, h.n_pad, np.int32),
             "lo": self._arr(r.lo_off, h.n_pad, np.int32),
             "hi": self._arr(r.hi_off, h.n_pad, np.int32),
+            "pre": (self._arr(r.pre_off, h.n_pad, np.int32) if r.pre_off
+                    else np.zeros(h.n_pad, dtype=np.int32)),
             "count": self._arr(r.count_off, h.n, np.int32),
             "row_ptr": self._arr(r.row_ptr_off, h.nqt + 1, np.int32),
             "col": self._arr(r.col_off, r.nnz, np.int32),

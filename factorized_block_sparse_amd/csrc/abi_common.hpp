@@ -16,6 +16,7 @@ struct LaunchInfo {
   int64_t fwd_sched_off, bwd_sched_off, total_bytes;
   int64_t fwd_xl_off, bwd_xl_off, fwd_xitem_off, bwd_xitem_off;
   int32_t fwd_xl_len, bwd_xl_len;
+  bool has_pre;  // some pattern's rows read a key prefix
 };
 
 inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -54,6 +55,12 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   li->bwd_xl_len = h.bwd_xl_len;
   li->fwd_xitem_off = h.fwd_xitem_off;
   li->bwd_xitem_off = h.bwd_xitem_off;
+  li->has_pre = false;
+  for (int32_t i = 0; i < h.num_patterns; ++i) {
+    sa_pattern_rec r;
+    memcpy(&r, static_cast<const uint8_t*>(blob_host) + h.pattern_off + i * sizeof(r), sizeof(r));
+    li->has_pre |= r.pre_off != 0;
+  }
   return SA_OK;
 }
 
@@ -75,6 +82,7 @@ inline void fill_pattern_table(const void* blob_host, const void* blob_dev, Tabl
     v.kmap = reinterpret_cast<const int32_t*>(db + r.kmap_off);
     v.lo = reinterpret_cast<const int32_t*>(db + r.lo_off);
     v.hi = reinterpret_cast<const int32_t*>(db + r.hi_off);
+    v.pre = r.pre_off ? reinterpret_cast<const int32_t*>(db + r.pre_off) : nullptr;
     v.row_ptr = reinterpret_cast<const int32_t*>(db + r.row_ptr_off);
     v.col = reinterpret_cast<const int32_t*>(db + r.col_off);
     v.fflag = db + r.fflag_off;

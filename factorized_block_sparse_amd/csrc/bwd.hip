@@ -65,7 +65,7 @@ struct BwdParams {
 // --------------------------------------------------------------------------
 // dQ pass: one workgroup per query tile, BQ = 32 * NW rows, key tiles of BK.
 // --------------------------------------------------------------------------
-template <int BQ, int BK>
+template <int BQ, int BK, bool PRE>
 __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NKB = BK / 32;
@@ -89,6 +89,9 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const int prow = qt * BQ + w * 32 + l32;
   const int tok = pv.qmap[prow];
   const int lo = pv.lo[prow], hi = pv.hi[prow];
+  // PRE: some pattern of the layout has key prefixes; this head's pattern may
+  // still have none (no array).
+  const int pre = (PRE && pv.pre) ? pv.pre[prow] : 0;
 
   bf16x8 qf[4], dof[4];
   float dsum = 0.f, lse2 = 0.f;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
       if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
-    const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
+    const bool mine = ((lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0)) || (PRE && pre > k0);
     // One tile; IS_FULL is a compile-time copy of the tile's FULL flag so the
     // element loops carry no branch.
     auto tile = [&](auto full_tag) {
@@ -182,13 +185,14 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
         }
         // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
         const int lo_rel = lo - k0 - 32 * kb - 8 * g, hi_rel = hi - k0 - 32 * kb - 8 * g;
+        const int pre_rel = pre - k0 - 32 * kb - 8 * g;
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fast_exp2(fmaf(s[r], c2, -lse2));
           if (!IS_FULL) {
             const int cr = 16 * (r >> 3) + (r & 7);  // key offset beyond 32*kb + 8*g
-            pr = (cr >= lo_rel && cr <= hi_rel) ? pr : 0.f;
+            pr = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? pr : 0.f;
           }
           ds[r] = pr * dp[r];
         }
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 // BK = 32 * NW keys; query tiles of BQ rows are processed in steps of
 // QS = min(BQ, 64) rows.
 // --------------------------------------------------------------------------
-template <int BQ, int BK>
+template <int BQ, int BK, bool PRE>
 __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
   constexpr int QS = BQ < 64 ? BQ : 64;
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float snd[2][QS];
   __shared__ __attribute__((aligned(16))) int32_t slo[2][QS];
   __shared__ __attribute__((aligned(16))) int32_t shi[2][QS];
+  __shared__ __attribute__((aligned(16))) int32_t spre[2][QS];  // only for patterns with prefixes
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -315,7 +320,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const bf16* dgl = p.dout + base * kD;
   const int drow = lane >> 3;
   float lse_r = 0.f, dd_r = 0.f;
-  int lo_r = 1, hi_r = 0;
+  int lo_r = 1, hi_r = 0, pre_r = 0;
+  const bool has_pre = PRE && pv.pre != nullptr;
   int qidx[IPW], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
   TileWindow win = tile_window(pv.row, pv.bflag, c0, c1);
   auto iload = [&](int step) {
@@ -344,6 +350,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       if ((ent & 1) == 0) {
         lo_r = pv.lo[r];
         hi_r = pv.hi[r];
+        if (has_pre) pre_r = pv.pre[r];
       }
       lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : INFINITY;
       dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
@@ -355,6 +362,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       snd[buf][tid] = -dd_r;
       slo[buf][tid] = lo_r;
       shi[buf][tid] = hi_r;
+      if (has_pre) spre[buf][tid] = pre_r;
     }
   };
 
@@ -405,12 +413,18 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
           const int4 lob = *reinterpret_cast<const int4*>(&slo[buf][qloc + 4]);
           const int4 hia = *reinterpret_cast<const int4*>(&shi[buf][qloc]);
           const int4 hib = *reinterpret_cast<const int4*>(&shi[buf][qloc + 4]);
+          int4 pra = int4{0, 0, 0, 0}, prb = int4{0, 0, 0, 0};
+          if (has_pre) {
+            pra = *reinterpret_cast<const int4*>(&spre[buf][qloc]);
+            prb = *reinterpret_cast<const int4*>(&spre[buf][qloc + 4]);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int qlo = j < 4 ? loa[j] : lob[j - 4];
             const int qhi = j < 4 ? hia[j] : hib[j - 4];
+            const int qpre = j < 4 ? pra[j] : prb[j - 4];
             const int r = 8 * h8 + j;
-            s[r] = (kpos >= qlo && kpos <= qhi) ? s[r] : -INFINITY;
+            s[r] = ((PRE && kpos < qpre) || (kpos >= qlo && kpos <= qhi)) ? s[r] : -INFINITY;
           }
         }
       }
@@ -652,21 +666,28 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
 
 #define SA_LAUNCH(kern, grid, threads) \
   hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(threads), 0, st, prm)
+// Kernels for layouts with key prefixes are separate instantiations, so the
+// other layouts run code without the prefix compares.
+#define SA_LAUNCH_P(KN, A, C, g, threads)               \
+  do {                                                  \
+    if (li.has_pre) SA_LAUNCH((KN<A, C, true>), g, threads); \
+    else SA_LAUNCH((KN<A, C, false>), g, threads);      \
+  } while (0)
   if ((phases & SA_BWD_DQ) && gq > 0) {
-    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_dq_kernel<32, 32>), gq, 64);
-    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_dq_kernel<32, 64>), gq, 64);
-    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_dq_kernel<64, 32>), gq, 128);
-    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_dq_kernel<64, 64>), gq, 128);
-    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_dq_kernel<128, 32>), gq, 256);
-    else SA_LAUNCH((bwd_dq_kernel<128, 64>), gq, 256);
+    if (bq == 32 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 32, 32, gq, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH_P(bwd_dq_kernel, 32, 64, gq, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 64, 32, gq, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH_P(bwd_dq_kernel, 64, 64, gq, 128);
+    else if (bq == 128 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 128, 32, gq, 256);
+    else SA_LAUNCH_P(bwd_dq_kernel, 128, 64, gq, 256);
   }
   if ((phases & SA_BWD_DKDV) && gk > 0) {
-    if (bq == 32 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<32, 32>), gk, 64);
-    else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<64, 32>), gk, 64);
-    else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_dkdv_kernel<128, 32>), gk, 64);
-    else if (bq == 32 && bk == 64) SA_LAUNCH((bwd_dkdv_kernel<32, 64>), gk, 128);
-    else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_dkdv_kernel<64, 64>), gk, 128);
-    else SA_LAUNCH((bwd_dkdv_kernel<128, 64>), gk, 128);
+    if (bq == 32 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 32, 32, gk, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 64, 32, gk, 64);
+    else if (bq == 128 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 128, 32, gk, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH_P(bwd_dkdv_kernel, 32, 64, gk, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH_P(bwd_dkdv_kernel, 64, 64, gk, 128);
+    else SA_LAUNCH_P(bwd_dkdv_kernel, 128, 64, gk, 128);
   }
   if ((phases & SA_BWD_MERGE) && gm > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH((bwd_merge_kernel<32, 32>), gm, 256);
@@ -676,6 +697,7 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_merge_kernel<128, 32>), gm, 256);
     else SA_LAUNCH((bwd_merge_kernel<128, 64>), gm, 256);
   }
+#undef SA_LAUNCH_P
 #undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;
 }

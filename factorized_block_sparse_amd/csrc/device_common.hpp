@@ -175,6 +175,7 @@ struct PatView {
   const int32_t* kmap;
   const int32_t* lo;
   const int32_t* hi;
+  const int32_t* pre;  // key prefix [0, pre[p]) of each row; nullptr = all empty
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* fflag;
@@ -192,6 +193,7 @@ __device__ __forceinline__ PatView pattern_of_index(const uint8_t* blob, int pi)
   v.kmap = reinterpret_cast<const int32_t*>(blob + rec->kmap_off);
   v.lo = reinterpret_cast<const int32_t*>(blob + rec->lo_off);
   v.hi = reinterpret_cast<const int32_t*>(blob + rec->hi_off);
+  v.pre = rec->pre_off ? reinterpret_cast<const int32_t*>(blob + rec->pre_off) : nullptr;
   v.row_ptr = reinterpret_cast<const int32_t*>(blob + rec->row_ptr_off);
   v.col = reinterpret_cast<const int32_t*>(blob + rec->col_off);
   v.fflag = blob + rec->fflag_off;

@@ -11,8 +11,8 @@
 //      V^T reaches the MFMA through transposing LDS reads;
 //   2. each wave owns 32 query rows and computes S^T = K Q^T on the MFMA
 //      units (fp32 accumulation; Q stays in registers for the whole walk);
-//   3. on PARTIAL tiles the fine mask is two integer compares against the
-//      row's key interval; FULL tiles apply no mask;
+//   3. on PARTIAL tiles the fine mask is a few integer compares against the
+//      row's key prefix and interval; FULL tiles apply no mask;
 //   4. running max update in base 2 with the softmax scale folded into one
 //      FMA per score; the running max (and the rescale of the accumulators)
 //      only moves when a tile's max exceeds it by more than 2^kRescaleLog2,
@@ -153,7 +153,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 
 // Occupancy target 3 waves per SIMD: the register allocation then leaves the
 // scheduler room to overlap the next tile's LDS reads and MFMAs with the
 // softmax (measured faster than the 4 waves the kernel could fit).
-template <int BQ, int BK>
+template <int BQ, int BK, bool PRE>
 __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ >= 64 ? 3 : 2, BQ >= 64 ? 3 : 2)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
@@ -182,6 +182,9 @@ void fwd_bf16_kernel(FwdParams p) {
   const int prow = qt * BQ + w * 32 + l32;
   const int tok = pv.qmap[prow];
   const int lo = pv.lo[prow], hi = pv.hi[prow];
+  // PRE: some pattern of the layout has key prefixes; this head's pattern may
+  // still have none (no array).
+  const int pre = (PRE && pv.pre) ? pv.pre[prow] : 0;
 
   bf16x8 qf[4];
   if (tok >= 0) {
@@ -242,7 +245,7 @@ void fwd_bf16_kernel(FwdParams p) {
       if (it + 2 < e1) iload(win.get(it + 2) >> 1);    // indices of tile it+2
     }
     const int k0 = kt * BK;
-    const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
+    const bool mine = ((lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0)) || (PRE && pre > k0);
     if (__any(mine)) {
       floatx16 s[NKB];
 #pragma unroll
@@ -255,15 +258,15 @@ void fwd_bf16_kernel(FwdParams p) {
                             s[kb]);
       }
       if (!full) {
-        // Key k0 + c is visible iff lo <= k0 + c <= hi; c = 32*kb + kappa(r, g)
-        // = 8*g + (a constant per register).
-        const int lo_rel = lo - k0 - 8 * g, hi_rel = hi - k0 - 8 * g;
+        // Key k0 + c is visible iff k0 + c < pre or lo <= k0 + c <= hi;
+        // c = 32*kb + kappa(r, g) = 8*g + (a constant per register).
+        const int lo_rel = lo - k0 - 8 * g, hi_rel = hi - k0 - 8 * g, pre_rel = pre - k0 - 8 * g;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int cr = 32 * kb + 16 * (r >> 3) + (r & 7);
-            s[kb][r] = (cr >= lo_rel && cr <= hi_rel) ? s[kb][r] : -INFINITY;
+            s[kb][r] = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? s[kb][r] : -INFINITY;
           }
       }
       float mx = -INFINITY;  // max of the raw scores (scale > 0)
@@ -321,7 +324,7 @@ void fwd_bf16_kernel(FwdParams p) {
 // --------------------------------------------------------------------------
 // float32 inputs, 32x32x2 f32 MFMA (same structure; K slot = one feature)
 // --------------------------------------------------------------------------
-template <int BQ, int BK>
+template <int BQ, int BK, bool PRE>
 __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
@@ -348,6 +351,9 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
   const int prow = qt * BQ + w * 32 + l32;
   const int tok = pv.qmap[prow];
   const int lo = pv.lo[prow], hi = pv.hi[prow];
+  // PRE: some pattern of the layout has key prefixes; this head's pattern may
+  // still have none (no array).
+  const int pre = (PRE && pv.pre) ? pv.pre[prow] : 0;
 
   float qf[32];
 #pragma unroll
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
     const bool full = pv.fflag[it] == SA_TILE_FULL;
     if (it + 1 < e1) gload(pv.col[it + 1]);
     const int k0 = kt * BK;
-    const bool mine = (lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0);
+    const bool mine = ((lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0)) || (PRE && pre > k0);
     if (__any(mine)) {
       floatx16 s[NKB];
 #pragma unroll
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kp = k0 + 32 * kb + kappa32(r, g);
-          const float x = (full || (kp >= lo && kp <= hi)) ? s[kb][r] * c2 : kMasked;
+          const float x = (full || (PRE && kp < pre) || (kp >= lo && kp <= hi)) ? s[kb][r] * c2 : kMasked;
           s[kb][r] = x;
           mx = fmaxf(mx, x);
         }
@@ -569,18 +575,25 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
   (void)hipGetLastError();
 #define SA_LAUNCH(kern, g, threads) \
   hipLaunchKernelGGL(kern, dim3(unsigned(g)), dim3(threads), 0, st, prm)
+// Kernels for layouts with key prefixes are separate instantiations, so the
+// other layouts run code without the prefix compares.
+#define SA_LAUNCH_P(KN, A, C, g, threads)               \
+  do {                                                  \
+    if (li.has_pre) SA_LAUNCH((KN<A, C, true>), g, threads); \
+    else SA_LAUNCH((KN<A, C, false>), g, threads);      \
+  } while (0)
   if (phases & SA_FWD_MAIN) {
     if (dtype == SA_BF16) {
-      if (bq == 32 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<32, 32>), grid, 64);
-      else if (bq == 32 && bk == 64) SA_LAUNCH((fwd_bf16_kernel<32, 64>), grid, 64);
-      else if (bq == 64 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<64, 32>), grid, 128);
-      else if (bq == 64 && bk == 64) SA_LAUNCH((fwd_bf16_kernel<64, 64>), grid, 128);
-      else if (bq == 128 && bk == 32) SA_LAUNCH((fwd_bf16_kernel<128, 32>), grid, 256);
-      else SA_LAUNCH((fwd_bf16_kernel<128, 64>), grid, 256);
+      if (bq == 32 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 32, 32, grid, 64);
+      else if (bq == 32 && bk == 64) SA_LAUNCH_P(fwd_bf16_kernel, 32, 64, grid, 64);
+      else if (bq == 64 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 64, 32, grid, 128);
+      else if (bq == 64 && bk == 64) SA_LAUNCH_P(fwd_bf16_kernel, 64, 64, grid, 128);
+      else if (bq == 128 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 128, 32, grid, 256);
+      else SA_LAUNCH_P(fwd_bf16_kernel, 128, 64, grid, 256);
     } else {
-      if (bq == 32) SA_LAUNCH((fwd_f32_kernel<32, 32>), grid, 64);
-      else if (bq == 64) SA_LAUNCH((fwd_f32_kernel<64, 32>), grid, 128);
-      else SA_LAUNCH((fwd_f32_kernel<128, 32>), grid, 256);
+      if (bq == 32) SA_LAUNCH_P(fwd_f32_kernel, 32, 32, grid, 64);
+      else if (bq == 64) SA_LAUNCH_P(fwd_f32_kernel, 64, 32, grid, 128);
+      else SA_LAUNCH_P(fwd_f32_kernel, 128, 32, grid, 256);
     }
   }
   if ((phases & SA_FWD_MERGE) && mgrid > 0) {
@@ -594,6 +607,7 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
       else SA_LAUNCH((fwd_merge_kernel<float, 128>), mgrid, 256);
     }
   }
+#undef SA_LAUNCH_P
 #undef SA_LAUNCH
   return hipGetLastError() == hipSuccess ? SA_OK : SA_EHIP;
 }

@@ -10,16 +10,23 @@
 // visible pair are computed; a fine mask applies inside partial tiles).
 //
 // Each pattern is mapped to a "layout space" in which every query row reads a
-// single interval of key positions:
+// prefix [0, pre) and a single interval [lo, hi] of key positions:
 //   local, same-block: identity order, interval [max(0,i-l), i] or [l*floor(i/l), i];
 //   stride: residue-class order (the grid-column view of the comparison
 //           article "稀疏与局部注意力", section 2), interval = the row's own
 //           class up to itself;
 //   summary: keys packed as the summary cells in order, so a row reads a
 //           prefix of them; rows that read nothing (before the first summary
-//           cell) read a key slot holding their own token.
-// This is what makes tiles dense for the stride and summary heads instead of
-// holding one useful key per row.
+//           cell) read a key slot holding their own token;
+//   merged fixed (report section 3.1, Eq. 7: one head reads both fixed sets):
+//           the summary cells packed first, so a row's cells up to itself are
+//           a prefix; the other tokens follow in order, so the rest of its
+//           block up to itself is an interval;
+//   local + global tokens (blog post sections 03, 04): identity order, the
+//           global tokens before the window as the prefix.
+// The prefix is empty for the first four kinds.  This is what makes tiles
+// dense for the stride and summary heads instead of holding one useful key
+// per row.
 
 #include <algorithm>
 #include <cstdint>
@@ -39,7 +46,7 @@ struct Pattern {
   sa_head_pattern p{};
   int32_t s = 0;
   int64_t pairs = 0;
-  std::vector<int32_t> qmap, kmap, lo, hi, count;
+  std::vector<int32_t> qmap, kmap, lo, hi, pre, count;  // pre: empty = no prefixes
   std::vector<int32_t> row_ptr, col, col_ptr, row;
   std::vector<uint8_t> fflag, bflag;
 };
@@ -47,23 +54,28 @@ struct Pattern {
 bool valid_tile(int32_t t) { return t == 32 || t == 64 || t == 128; }
 
 // Canonical form of a head pattern so that equal patterns share one record.
+bool has_summary(int32_t kind) { return kind == SA_SUMMARY || kind == SA_FIXED_MERGED; }
+
 sa_head_pattern canonical(const sa_head_pattern& h) {
   sa_head_pattern c = h;
-  if (h.kind != SA_SUMMARY) {
-    c.c = 0;
+  if (has_summary(h.kind)) {
+    c.sub = h.sub % (h.l / h.c);
+  } else if (h.kind == SA_LOCAL_GLOBAL) {
     c.sub = 0;
   } else {
-    c.sub = h.sub % (h.l / h.c);
+    c.c = 0;
+    c.sub = 0;
   }
   return c;
 }
 
 int check_head(const sa_head_pattern& h) {
-  if (h.kind < SA_LOCAL || h.kind > SA_SUMMARY) return SA_EINVAL;
+  if (h.kind < SA_LOCAL || h.kind > SA_LOCAL_GLOBAL) return SA_EINVAL;
   if (h.l < 1) return SA_EINVAL;
-  if (h.kind == SA_SUMMARY) {
+  if (has_summary(h.kind)) {
     if (h.c < 1 || h.c > h.l || h.sub < 0) return SA_EINVAL;
   }
+  if (h.kind == SA_LOCAL_GLOBAL && h.c < 0) return SA_EINVAL;
   return SA_OK;
 }
 
@@ -140,12 +152,56 @@ int build_maps(Pattern& P, int64_t n64, int32_t n_pad, bool self_if_empty) {
       if (e != n) return SA_EINVAL;
       break;
     }
+    case SA_FIXED_MERGED: {
+      const int32_t c = P.p.c;
+      const int32_t s = l - (P.p.sub + 1) * c;
+      P.s = s;
+      P.pre.assign(n_pad, 0);
+      auto is_cell = [&](int32_t j) { return j % l >= s && j % l < s + c; };
+      std::vector<int32_t> pos(n, -1);  // key position of each non-summary token
+      int32_t e = 0;
+      for (int32_t j = 0; j < n; ++j)
+        if (is_cell(j)) P.kmap[e++] = j;
+      for (int32_t j = 0; j < n; ++j)
+        if (!is_cell(j)) {
+          pos[j] = e;
+          P.kmap[e++] = j;
+        }
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t b = i / l, r = i % l;
+        P.qmap[i] = i;
+        P.pre[i] = b * c + std::min(std::max(r - s + 1, 0), c);  // cells j <= i
+        // The block's other tokens up to i: from its first non-cell token to
+        // the last non-cell token <= i (consecutive key positions).
+        const int32_t first = s > 0 ? b * l : b * l + c;
+        const int32_t last = is_cell(i) ? b * l + s - 1 : i;
+        if (first <= last) {
+          P.lo[i] = pos[first];
+          P.hi[i] = pos[last];
+        }
+      }
+      break;
+    }
+    case SA_LOCAL_GLOBAL: {
+      const int32_t glob = P.p.c;
+      P.pre.assign(n_pad, 0);
+      for (int32_t i = 0; i < n; ++i) {
+        P.qmap[i] = P.kmap[i] = i;
+        P.lo[i] = i > l ? i - l : 0;
+        P.hi[i] = i;
+        P.pre[i] = std::min(glob, P.lo[i]);  // global tokens before the window
+      }
+      break;
+    }
     default:
       return SA_EINVAL;
   }
+  bool any_pre = false;
+  for (int32_t v : P.pre) any_pre |= v > 0;
+  if (!any_pre) P.pre.clear();
   P.pairs = 0;
   for (int32_t p = 0; p < n; ++p) {
-    const int32_t cnt = P.hi[p] - P.lo[p] + 1;
+    const int32_t cnt = std::max(P.hi[p] - P.lo[p] + 1, 0) + (P.pre.empty() ? 0 : P.pre[p]);
     P.count[P.qmap[p]] = cnt;
     P.pairs += cnt;
   }
@@ -163,21 +219,38 @@ void build_tiles(Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
     const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, n);
     int32_t max_lo = INT32_MIN, min_hi = INT32_MAX;
     touched.clear();
+    auto touch = [&](int32_t kt) {
+      if (!mark[kt]) {
+        mark[kt] = 1;
+        touched.push_back(kt);
+      }
+    };
     for (int32_t r = r0; r < r1; ++r) {
       const int32_t lo = P.lo[r], hi = P.hi[r];
       max_lo = std::max(max_lo, lo);
       min_hi = std::min(min_hi, hi);
-      for (int32_t kt = lo / bk; kt <= hi / bk; ++kt) {
-        if (!mark[kt]) {
-          mark[kt] = 1;
-          touched.push_back(kt);
-        }
-      }
+      if (lo <= hi)
+        for (int32_t kt = lo / bk; kt <= hi / bk; ++kt) touch(kt);
+      if (!P.pre.empty() && P.pre[r] > 0)
+        for (int32_t kt = 0; kt <= (P.pre[r] - 1) / bk; ++kt) touch(kt);
     }
     std::sort(touched.begin(), touched.end());
     const bool rows_all_valid = (r0 + bq <= n);
+    // Every key of [a, b] visible to row r: inside the prefix, or inside the
+    // interval (extended to 0 when the prefix reaches it).
+    auto covered = [&](int32_t r, int32_t a, int32_t b) {
+      const int32_t pre = P.pre[r], lo = P.lo[r], hi = P.hi[r];
+      if (b < pre) return true;
+      if (lo > hi) return false;
+      return a >= (pre >= lo ? 0 : lo) && b <= hi;
+    };
     for (int32_t kt : touched) {
-      const bool full = rows_all_valid && kt * bk >= max_lo && (kt + 1) * bk - 1 <= min_hi;
+      bool full = rows_all_valid;
+      if (full && P.pre.empty()) {
+        full = kt * bk >= max_lo && (kt + 1) * bk - 1 <= min_hi;
+      } else {
+        for (int32_t r = r0; full && r < r1; ++r) full = covered(r, kt * bk, (kt + 1) * bk - 1);
+      }
       P.col.push_back(kt);
       P.fflag.push_back(full ? SA_TILE_FULL : SA_TILE_PARTIAL);
       mark[kt] = 0;
@@ -425,6 +498,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       r.kmap_off = w.put(P.kmap);
       r.lo_off = w.put(P.lo);
       r.hi_off = w.put(P.hi);
+      r.pre_off = P.pre.empty() ? 0 : w.put(P.pre);
       r.count_off = w.put(P.count);
       r.row_ptr_off = w.put(P.row_ptr);
       r.col_off = w.put(P.col);
@@ -525,6 +599,7 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
     const int64_t np = 4 * int64_t(h.n_pad);
     if (!in_blob(r.qmap_off, np, total) || !in_blob(r.kmap_off, np, total) ||
         !in_blob(r.lo_off, np, total) || !in_blob(r.hi_off, np, total) ||
+        (r.pre_off != 0 && !in_blob(r.pre_off, np, total)) ||
         !in_blob(r.count_off, 4 * h.n, total) ||
         !in_blob(r.row_ptr_off, 4 * int64_t(h.nqt + 1), total) ||
         !in_blob(r.col_off, 4 * int64_t(r.nnz), total) ||

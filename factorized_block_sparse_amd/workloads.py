@@ -33,6 +33,8 @@ LOCAL = "local"
 STRIDE = "stride"
 SAMEBLOCK = "sameblock"
 SUMMARY = "summary"
+FIXED_MERGED = "fixed_merged"
+LOCAL_GLOBAL = "local_global"
 
 
 @dataclass(frozen=True)
@@ -65,6 +67,11 @@ def strided_heads(H: int, l: int) -> tuple:
     return tuple(HeadSpec(LOCAL, l) if h % 2 == 0 else HeadSpec(STRIDE, l) for h in range(H))
 
 
+def merged_heads(H: int, l: int, c: int) -> tuple:
+    """Merged fixed heads (report section 3.1, Eq. 7): head k reads its block and sub-block k's cells."""
+    return tuple(HeadSpec(FIXED_MERGED, l, c, h) for h in range(H))
+
+
 def fixed_heads(H: int, l: int, c: int) -> tuple:
     """Alternating same-block / summary heads; summary head k uses sub-block k."""
     return tuple(HeadSpec(SAMEBLOCK, l) if h % 2 == 0 else HeadSpec(SUMMARY, l, c, h // 2)
@@ -88,6 +95,12 @@ WORKLOADS = {
         Workload("fixed_c8_n12288", 2, 8, 12288, 64, fixed_heads(8, 128, 8), "bf16", 128, 64, 1006,
                  note="fixed pattern with narrow summaries (l=128, c=8, the report's own example); "
                       "the summary cells of consecutive blocks are packed into dense key tiles"),
+        Workload("fixed_merged_n12288", 2, 8, 12288, 64, merged_heads(8, 128, 32), "bf16", 128, 64,
+                 1007, note="merged fixed heads at the Enwik8 context length (the report's Enwik8 "
+                            "model: fixed pattern, l=128, c=32, merged heads), head k on sub-block k"),
+        Workload("local_global_n12288", 2, 8, 12288, 64,
+                 tuple(HeadSpec(LOCAL_GLOBAL, 256, 64) for _ in range(8)), "bf16", 64, 64, 1008,
+                 note="causal window of 256 plus 64 leading global tokens (blog post sections 03-04)"),
         Workload("strided_n65536", 1, 8, 65536, 64, strided_heads(8, 256), "bf16", 64, 64, 1005,
                  note="long strided pattern at the audio length 65,536"),
     )

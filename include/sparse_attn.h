@@ -13,6 +13,11 @@
  *     SA_SAMEBLOCK  fixed head 1:    {j <= i : floor(j / l) == floor(i / l)}
  *     SA_SUMMARY    fixed head 2:    {j <= i : s <= j mod l <= s + c - 1},
  *                   s = l - (k + 1) c for sub-block k = sub mod (l / c)
+ *     SA_FIXED_MERGED  one head reading the union of the two fixed sets (the
+ *                   merged integration of report section 3.1, Eq. 7)
+ *     SA_LOCAL_GLOBAL  {j <= i : i - j <= l or j < c}: the causal window plus
+ *                   the first c positions as global tokens (blog post sections
+ *                   03 and 04)
  * Rows left empty by a summary head (i < s) read only themselves when
  * SA_SELF_IF_EMPTY is set (the default reading; without it such a layout is
  * rejected, since an empty row has no softmax).  Execution is at tile
@@ -59,7 +64,14 @@ enum sa_status {
   SA_EHIP = -4           /* the HIP runtime reported an error at launch */
 };
 
-enum sa_head_kind { SA_LOCAL = 0, SA_STRIDE = 1, SA_SAMEBLOCK = 2, SA_SUMMARY = 3 };
+enum sa_head_kind {
+  SA_LOCAL = 0,
+  SA_STRIDE = 1,
+  SA_SAMEBLOCK = 2,
+  SA_SUMMARY = 3,
+  SA_FIXED_MERGED = 4,
+  SA_LOCAL_GLOBAL = 5
+};
 
 enum sa_dtype { SA_BF16 = 0, SA_FP32 = 1 };
 
@@ -67,11 +79,13 @@ enum sa_dtype { SA_BF16 = 0, SA_FP32 = 1 };
  * no rule; the blog post's section 02 forbids empty rows). */
 #define SA_SELF_IF_EMPTY 1u
 
-/* One head's pattern.  c and sub are used by SA_SUMMARY only. */
+/* One head's pattern.  c is the summary width (SA_SUMMARY, SA_FIXED_MERGED)
+ * or the number of leading global tokens (SA_LOCAL_GLOBAL); sub is used by
+ * SA_SUMMARY and SA_FIXED_MERGED only. */
 typedef struct {
   int32_t kind;  /* enum sa_head_kind */
   int32_t l;     /* band width / stride / block length, >= 1 */
-  int32_t c;     /* summary width, 1 <= c <= l */
+  int32_t c;     /* summary width, 1 <= c <= l; or global tokens, >= 0 */
   int32_t sub;   /* summary sub-block index, >= 0 (taken mod l / c) */
 } sa_head_pattern;
 
@@ -102,9 +116,16 @@ typedef struct {
  *   SA_SUMMARY: queries identity; keys are the summary cells in increasing
  *     order, then the tokens of rows that read only themselves, then every
  *     other token (keys nobody reads: their dK/dV are zero).
- * In layout space every query row reads one interval of key positions,
- * [lo[p], hi[p]] (lo > hi only on padding rows), which is what makes the
- * per-tile fine mask two comparisons.  Tiles: q-tile i covers positions
+ *   SA_FIXED_MERGED: queries identity; keys are the summary cells in
+ *     increasing order, then every other token in increasing order.
+ *   SA_LOCAL_GLOBAL: identity.
+ * In layout space every query row reads a prefix and one interval of key
+ * positions, [0, pre[p]) and [lo[p], hi[p]], with pre[p] <= lo[p] when the
+ * interval is not empty (lo > hi: empty).  The prefix is empty except for
+ * SA_FIXED_MERGED (a row's summary cells up to itself; the interval holds
+ * the other tokens of its block up to itself) and SA_LOCAL_GLOBAL (global
+ * tokens before the window).  This is what makes the per-tile fine mask a
+ * few comparisons.  Tiles: q-tile i covers positions
  * [i*block_q, (i+1)*block_q), k-tile j covers [j*block_k, (j+1)*block_k).  A
  * tile pair is active iff it holds a visible pair, FULL iff every pair in it
  * is visible.  CSR lists each q-tile's active k-tiles (ascending), CSC each
@@ -112,7 +133,7 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 7u
+#define SA_BLOB_VERSION 8u
 #define SA_SCHED_FIELDS 8
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
@@ -138,6 +159,7 @@ typedef struct {
   int64_t kmap_off;    /* int32[n_pad] */
   int64_t lo_off;      /* int32[n_pad] */
   int64_t hi_off;      /* int32[n_pad] */
+  int64_t pre_off;     /* int32[n_pad]; 0 when every prefix is empty */
   int64_t count_off;   /* int32[n]: visible keys of token i (token order) */
   int64_t row_ptr_off; /* int32[nqt + 1] */
   int64_t col_off;     /* int32[nnz]: k-tile of each CSR entry */

@@ -101,9 +101,10 @@ def visible(kind: str, i, j, l: int, c: int | None = None, sub: int = 0):
     if kind == FIXED_MERGED:
         return visible(SAMEBLOCK, i, j, l) | visible(SUMMARY, i, j, l, c, sub)
     if kind == LOCAL_GLOBAL:
-        if c is None or c < 0:
+        g = 0 if c is None else c  # None: no global tokens
+        if g < 0:
             raise ValueError("need a number of global tokens c >= 0")
-        return causal & ((i - j <= l) | (j < c))
+        return causal & ((i - j <= l) | (j < g))
     raise ValueError(f"unknown head kind {kind!r}")
 
 
@@ -150,9 +151,10 @@ def row_keys(kind: str, i: int, n: int, l: int, c: int | None = None,
         keys = np.union1d(row_keys(SAMEBLOCK, i, n, l),
                           row_keys(SUMMARY, i, n, l, c, sub, self_if_empty=False))
     elif kind == LOCAL_GLOBAL:
-        if c is None or c < 0:
+        g = 0 if c is None else c
+        if g < 0:
             raise ValueError("need a number of global tokens c >= 0")
-        keys = np.union1d(np.arange(0, min(c, i + 1), dtype=np.int64),
+        keys = np.union1d(np.arange(0, min(g, i + 1), dtype=np.int64),
                           np.arange(max(0, i - l), i + 1, dtype=np.int64))
     else:
         raise ValueError(f"unknown head kind {kind!r}")

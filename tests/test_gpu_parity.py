@@ -41,6 +41,22 @@ SMALL = [
     ("split_q128_k64", 1, 2200, 128, 64, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
                                           HeadPattern("sameblock", 2048)], 1024),
     ("split_default_caps", 1, 2600, 64, 64, [HeadPattern("local", 2500), HeadPattern("summary", 64, 16, 2)]),
+    # heads whose rows read a key prefix besides an interval (merged fixed; local + global tokens)
+    ("merged_global_tiles64", 2, 700, 64, 64, [HeadPattern("fixed_merged", 128, 32, 0),
+                                               HeadPattern("fixed_merged", 128, 32, 3),
+                                               HeadPattern("local_global", 64, 16),
+                                               HeadPattern("local_global", 100, 0)]),
+    ("merged_global_ragged", 1, 333, 64, 32, [HeadPattern("fixed_merged", 20, 3, 1),
+                                              HeadPattern("fixed_merged", 8, 8, 0),
+                                              HeadPattern("local_global", 17, 5),
+                                              HeadPattern("local_global", 3, 64)]),
+    ("merged_global_q128_k64", 1, 640, 128, 64, [HeadPattern("fixed_merged", 64, 8, 1),
+                                                 HeadPattern("local_global", 32, 40)]),
+    ("merged_global_tiles32", 1, 300, 32, 32, [HeadPattern("fixed_merged", 10, 1, 4),
+                                               HeadPattern("local_global", 500, 2),
+                                               HeadPattern("local_global", 1, 1000)]),
+    ("split_merged_global", 1, 2300, 64, 64, [HeadPattern("fixed_merged", 128, 32, 2),
+                                              HeadPattern("local_global", 256, 300)], 512),
 ]
 
 
@@ -189,7 +205,8 @@ def _sample_rows(n, l, rng, extra=6):
     return sorted(r for r in base if 0 <= r < n)
 
 
-@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "fixed_c8_n12288", "strided_n65536"])
+@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "fixed_c8_n12288", "strided_n65536",
+                                   "fixed_merged_n12288", "local_global_n12288"])
 def test_workload_full_size_sampled(wname):
     w = W.WORKLOADS[wname]
     lay = Layout(w.n, w.heads, w.block_q, w.block_k)

@@ -2,7 +2,7 @@
 
 The reference tiles are derived here, in test code: the documented index
 maps (identity; residue-class order for the stride head; summary cells first
-for the summary head) are rebuilt independently, the oracle's dense token
+for the summary and merged fixed heads) are rebuilt independently, the oracle's dense token
 mask is permuted by them, and a tile is active iff any entry in it is set and
 FULL iff all are.  CSR, CSC, flags, per-row intervals and per-token counts
 must match bit for bit.
@@ -27,8 +27,13 @@ def _doc_maps(kind, n, n_pad, l, c=0, sub=0):
     """Documented layout-space maps (query map, key map), -1 past n."""
     qmap = -np.ones(n_pad, dtype=np.int64)
     kmap = -np.ones(n_pad, dtype=np.int64)
-    if kind in ("local", "sameblock"):
+    if kind in ("local", "sameblock", "local_global"):
         qmap[:n] = kmap[:n] = np.arange(n)
+    elif kind == "fixed_merged":
+        s = M.summary_start(l, c, sub)
+        qmap[:n] = np.arange(n)
+        cells = [j for j in range(n) if s <= j % l <= s + c - 1]
+        kmap[:n] = cells + [j for j in range(n) if not s <= j % l <= s + c - 1]
     elif kind == "stride":
         order = sorted(range(n), key=lambda i: (i % l, i // l))
         qmap[:n] = kmap[:n] = order
@@ -73,6 +78,13 @@ CASES = [
     (97, 32, 64, [HeadPattern("stride", 10), HeadPattern("summary", 10, 1, 4)]),
     (1, 32, 32, [HeadPattern("local", 1), HeadPattern("summary", 4, 2, 0)]),
     (200, 64, 64, [HeadPattern("local", 500), HeadPattern("stride", 500), HeadPattern("summary", 8, 8, 0)]),
+    (512, 64, 64, [HeadPattern("fixed_merged", 128, 32, 0), HeadPattern("fixed_merged", 128, 32, 3),
+                   HeadPattern("local_global", 64, 16), HeadPattern("local_global", 100, 0)]),
+    (300, 64, 32, [HeadPattern("fixed_merged", 20, 3, 1), HeadPattern("fixed_merged", 8, 8, 0),
+                   HeadPattern("fixed_merged", 6, 1, 5), HeadPattern("local_global", 17, 5),
+                   HeadPattern("local_global", 3, 64), HeadPattern("local_global", 1, 1000)]),
+    (97, 32, 64, [HeadPattern("fixed_merged", 10, 1, 4), HeadPattern("local_global", 500, 2)]),
+    (1, 32, 32, [HeadPattern("fixed_merged", 4, 2, 0), HeadPattern("local_global", 4, 3)]),
 ]
 
 
@@ -94,10 +106,17 @@ def test_layout_bit_exact(n, bq, bk, heads):
         mask = M.head_mask(n, head.kind, head.l, head.c or None, head.sub)
         mp = np.zeros((n_pad, n_pad), dtype=bool)
         mp[:n, :n] = mask[np.ix_(qmap[:n], kmap[:n])]
-        # Every layout row reads exactly one interval [lo, hi].
+        # Every layout row reads exactly a prefix [0, pre) and one interval
+        # [lo, hi], the prefix before the interval.
         cols = np.arange(n_pad)
-        interval = (cols[None, :] >= arr["lo"][:, None]) & (cols[None, :] <= arr["hi"][:, None])
-        np.testing.assert_array_equal(interval, mp)
+        lo, hi, pre = arr["lo"], arr["hi"], arr["pre"]
+        interval = (cols[None, :] >= lo[:, None]) & (cols[None, :] <= hi[:, None])
+        np.testing.assert_array_equal(interval | (cols[None, :] < pre[:, None]), mp)
+        assert ((pre <= lo) | (lo > hi)).all()
+        if head.kind not in ("fixed_merged", "local_global"):
+            assert rec.pre_off == 0 and not pre.any()
+        # No prefix array at all when every prefix is empty (kernels must not read one).
+        assert (rec.pre_off == 0) == (not pre.any())
         np.testing.assert_array_equal(arr["count"], mask.sum(1))
         assert rec.pairs == mask.sum()
         total_pairs += int(mask.sum())

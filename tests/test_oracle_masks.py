@@ -151,6 +151,7 @@ def test_local_global_kind_is_the_worked_example(golden_dir):
                                   M.local_global_mask(50, 4, tuple(range(6))))
     # No global tokens: the local head of the strided pattern.
     np.testing.assert_array_equal(M.head_mask(30, M.LOCAL_GLOBAL, 3, 0), M.head_mask(30, M.LOCAL, 3))
+    np.testing.assert_array_equal(M.head_mask(30, M.LOCAL_GLOBAL, 3, None), M.head_mask(30, M.LOCAL, 3))
     with pytest.raises(ValueError):
         M.head_mask(10, M.LOCAL_GLOBAL, 3, -1)
 
