@@ -37,6 +37,8 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   // Element offsets of [B, H, n, d] must fit the kernels' 64-bit arithmetic and
   // per-(b, h) 32-bit row indices.
   if (int64_t(B) * H * h.n > (int64_t(1) << 40)) return SA_EUNSUPPORTED;
+  // bf16 kernels address a (b, h) slice with 32-bit byte offsets (128 B rows).
+  if (dtype == SA_BF16 && h.n >= (int64_t(1) << 25)) return SA_EUNSUPPORTED;
   li->n = h.n;
   li->block_q = h.block_q;
   li->block_k = h.block_k;

@@ -123,8 +123,8 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 
   // K, V tiles by direct loads, as in the forward; padding keys fetch token 0
   // (never visible: their probabilities, hence dS, are exactly 0).
-  const bf16* kg = p.k + base * kD;
-  const bf16* vg = p.v + base * kD;
+  const BufRsrc krs = slice_rsrc(p.k + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
+  const BufRsrc vrs = slice_rsrc(p.v + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
   const int drow = lane >> 3;
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
@@ -137,10 +137,9 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     bf16* vd = P ? v1s : v0s;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
-      const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
-      dma16(kg + off, kd + 8 * (w * IPW + i) * kD);
-      dma16(vg + off, vd + 8 * (w * IPW + i) * kD);
+      const uint32_t off = row_chunk_offset(kidx[i], (lane & 7) ^ swz_key(8 * (w * IPW + i) + drow));
+      dma16_buf(krs, off, kd + 8 * (w * IPW + i) * kD);
+      dma16_buf(vrs, off, vd + 8 * (w * IPW + i) * kD);
     }
   };
 
@@ -316,19 +315,23 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   // Q, dO rows by direct loads (swizzled tiles); per-row LSE, D and key
   // intervals through registers.  Padding query rows fetch token 0 and get
   // LSE = +inf, so their probabilities (hence dS) are exactly 0.
-  const bf16* qgl = p.q + base * kD;
-  const bf16* dgl = p.dout + base * kD;
+  const BufRsrc qrs = slice_rsrc(p.q + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
+  const BufRsrc drs = slice_rsrc(p.dout + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
   const int drow = lane >> 3;
   float lse_r = 0.f, dd_r = 0.f;
   int lo_r = 1, hi_r = 0, pre_r = 0;
   const bool has_pre = PRE && pv.pre != nullptr;
   int qidx[IPW], rtok = -1;  // query-map entries of the next step to load (fetched a step early)
+  // Per-row metadata: each wave loads and stores that of QS / NW rows.
+  constexpr int MPW = QS / NW;
+  const bool mthr = lane < MPW;
+  const int mrow = w * MPW + lane;
   TileWindow win = tile_window(pv.row, pv.bflag, c0, c1);
   auto iload = [&](int step) {
     const int r0 = (win.get(c0 + step / NSTEP) >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) qidx[i] = pv.qmap[r0 + 8 * (w * IPW + i) + drow];
-    if (tid < QS) rtok = pv.qmap[r0 + tid];
+    if (mthr) rtok = pv.qmap[r0 + mrow];
   };
   auto gload = [&](int step, auto par) {
     constexpr int P = decltype(par)::value;
@@ -338,13 +341,12 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     const int r0 = (ent >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
-      const size_t off = size_t(qidx[i] < 0 ? 0 : qidx[i]) * kD + dcol;
-      dma16(qgl + off, qd + 8 * (w * IPW + i) * kD);
-      dma16(dgl + off, od + 8 * (w * IPW + i) * kD);
+      const uint32_t off = row_chunk_offset(qidx[i], (lane & 7) ^ swz_key(8 * (w * IPW + i) + drow));
+      dma16_buf(qrs, off, qd + 8 * (w * IPW + i) * kD);
+      dma16_buf(drs, off, od + 8 * (w * IPW + i) * kD);
     }
-    if (tid < QS) {
-      const int r = r0 + tid;
+    if (mthr) {
+      const int r = r0 + mrow;
       const int tk = rtok;
       // Row intervals are read only by the masked body (PARTIAL tiles).
       if ((ent & 1) == 0) {
@@ -357,12 +359,12 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto mstore = [&](int buf) {
-    if (tid < QS) {
-      slse[buf][tid] = lse_r;
-      snd[buf][tid] = -dd_r;
-      slo[buf][tid] = lo_r;
-      shi[buf][tid] = hi_r;
-      if (has_pre) spre[buf][tid] = pre_r;
+    if (mthr) {
+      slse[buf][mrow] = lse_r;
+      snd[buf][mrow] = -dd_r;
+      slo[buf][mrow] = lo_r;
+      shi[buf][mrow] = hi_r;
+      if (has_pre) spre[buf][mrow] = pre_r;
     }
   };
 

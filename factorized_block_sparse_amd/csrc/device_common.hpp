@@ -112,6 +112,25 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
 }
 
+// The same direct load through a buffer resource over one (b, h) slice of a
+// [B, H, n, 64] bf16 tensor: the lane's source is a 32-bit byte offset into
+// the slice (one VALU operation) instead of a 64-bit address.  Offsets stay
+// below n * 128 bytes, which the host keeps under 2^32.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ BufRsrc slice_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), kBufWord3);
+}
+__device__ __forceinline__ void dma16_buf(BufRsrc r, uint32_t voff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16,
+                                           int(voff), 0, 0, 0);
+}
+// Byte offset of 16-byte chunk `chunk` of row `token` in a slice (clamped to
+// row 0 for padding entries, -1).
+__device__ __forceinline__ uint32_t row_chunk_offset(int token, int chunk) {
+  return uint32_t(token < 0 ? 0 : token) * uint32_t(kD * 2) + uint32_t(chunk) * 16u;
+}
+
 // s_waitcnt vmcnt(0): every global load of this wave (direct-to-LDS included)
 // has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -200,6 +200,8 @@ void fwd_bf16_kernel(FwdParams p) {
   // tile with its i-th direct load.  Padding keys (map entry -1) fetch token
   // 0 instead: they are never visible, so their probabilities are exactly 0.
   const int drow = lane >> 3;
+  const BufRsrc krs = slice_rsrc(kg, uint32_t(p.n) * uint32_t(kD * 2));
+  const BufRsrc vrs = slice_rsrc(vg, uint32_t(p.n) * uint32_t(kD * 2));
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
@@ -211,10 +213,9 @@ void fwd_bf16_kernel(FwdParams p) {
     bf16* vd = P ? v1s : v0s;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int dcol = ((lane & 7) ^ swz_key(8 * (w * IPW + i) + drow)) * 8;
-      const size_t off = size_t(kidx[i] < 0 ? 0 : kidx[i]) * kD + dcol;
-      dma16(kg + off, kd + 8 * (w * IPW + i) * kD);
-      dma16(vg + off, vd + 8 * (w * IPW + i) * kD);
+      const uint32_t off = row_chunk_offset(kidx[i], (lane & 7) ^ swz_key(8 * (w * IPW + i) + drow));
+      dma16_buf(krs, off, kd + 8 * (w * IPW + i) * kD);
+      dma16_buf(vrs, off, vd + 8 * (w * IPW + i) * kD);
     }
   };
 

@@ -29,7 +29,8 @@
  *     d innermost; LSE is [B, H, n] float32.  Head h uses the layout's
  *     pattern of head h; H must equal the layout's num_heads.
  *   - d must be 64.  dtype SA_BF16 (bfloat16 data, float32 accumulation)
- *     for forward and backward; SA_FP32 (float32 throughout) for forward.
+ *     for forward and backward, with n < 2^25 (SA_EUNSUPPORTED otherwise);
+ *     SA_FP32 (float32 throughout) for forward.
  *   - Pointers q, k, v, o, lse, dO, dq, dk, dv and workspace are device
  *     pointers (hipMalloc'd or equivalent) aligned to 16 bytes; blob_host is
  *     a host pointer; blob_dev is a device copy of the same bytes.
