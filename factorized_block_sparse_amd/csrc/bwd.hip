@@ -126,10 +126,11 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const BufRsrc krs = slice_rsrc(p.k + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
   const BufRsrc vrs = slice_rsrc(p.v + base * kD, uint32_t(p.n) * uint32_t(kD * 2));
   const int drow = lane >> 3;
+  const BufRsrc kmap_rs = array_rsrc(pv.kmap);
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
+    for (int i = 0; i < IPW; ++i) kidx[i] = buf_i32(kmap_rs, kt * BK + 8 * (w * IPW + i) + drow);
   };
   auto dload = [&](auto par) {
     constexpr int P = decltype(par)::value;
@@ -327,11 +328,13 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const bool mthr = lane < MPW;
   const int mrow = w * MPW + lane;
   TileWindow win = tile_window(pv.row, pv.bflag, c0, c1);
+  const BufRsrc qmap_rs = array_rsrc(pv.qmap), lo_rs = array_rsrc(pv.lo), hi_rs = array_rsrc(pv.hi);
+  const BufRsrc lse_rs = array_rsrc(p.lse + base), dsum_rs = array_rsrc(p.dsum + base);
   auto iload = [&](int step) {
     const int r0 = (win.get(c0 + step / NSTEP) >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) qidx[i] = pv.qmap[r0 + 8 * (w * IPW + i) + drow];
-    if (mthr) rtok = pv.qmap[r0 + mrow];
+    for (int i = 0; i < IPW; ++i) qidx[i] = buf_i32(qmap_rs, r0 + 8 * (w * IPW + i) + drow);
+    if (mthr) rtok = buf_i32(qmap_rs, r0 + mrow);
   };
   auto gload = [&](int step, auto par) {
     constexpr int P = decltype(par)::value;
@@ -350,12 +353,12 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       const int tk = rtok;
       // Row intervals are read only by the masked body (PARTIAL tiles).
       if ((ent & 1) == 0) {
-        lo_r = pv.lo[r];
-        hi_r = pv.hi[r];
+        lo_r = buf_i32(lo_rs, r);
+        hi_r = buf_i32(hi_rs, r);
         if (has_pre) pre_r = pv.pre[r];
       }
-      lse_r = tk >= 0 ? p.lse[base + tk] * kLog2e : INFINITY;
-      dd_r = tk >= 0 ? p.dsum[base + tk] : 0.f;
+      lse_r = tk >= 0 ? buf_f32(lse_rs, tk) * kLog2e : INFINITY;
+      dd_r = tk >= 0 ? buf_f32(dsum_rs, tk) : 0.f;
     }
   };
   auto mstore = [&](int buf) {

@@ -125,6 +125,19 @@ __device__ __forceinline__ void dma16_buf(BufRsrc r, uint32_t voff, void* lds_ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16,
                                            int(voff), 0, 0, 0);
 }
+// 32-bit loads through a buffer resource over an int32 / float array (the
+// blob's index arrays, a (b, h) slice of LSE or D): the lane's element is a
+// 32-bit byte offset.  No range is enforced (the callers index in bounds).
+__device__ __forceinline__ BufRsrc array_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), 0x7fffffff, kBufWord3);
+}
+__device__ __forceinline__ int buf_i32(BufRsrc r, int index) {
+  return int(__builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, 0));
+}
+__device__ __forceinline__ float buf_f32(BufRsrc r, int index) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, 0));
+}
+
 // Byte offset of 16-byte chunk `chunk` of row `token` in a slice (clamped to
 // row 0 for padding entries, -1).
 __device__ __forceinline__ uint32_t row_chunk_offset(int token, int chunk) {

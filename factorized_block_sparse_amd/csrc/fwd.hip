@@ -202,10 +202,11 @@ void fwd_bf16_kernel(FwdParams p) {
   const int drow = lane >> 3;
   const BufRsrc krs = slice_rsrc(kg, uint32_t(p.n) * uint32_t(kD * 2));
   const BufRsrc vrs = slice_rsrc(vg, uint32_t(p.n) * uint32_t(kD * 2));
+  const BufRsrc kmap_rs = array_rsrc(pv.kmap);
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) kidx[i] = pv.kmap[kt * BK + 8 * (w * IPW + i) + drow];
+    for (int i = 0; i < IPW; ++i) kidx[i] = buf_i32(kmap_rs, kt * BK + 8 * (w * IPW + i) + drow);
   };
   auto dload = [&](auto par) {
     constexpr int P = decltype(par)::value;
