@@ -37,6 +37,9 @@ local band.
 
 Two further head kinds combine sets in one head:
 
+* ``strided_merged``: one head reads the union of the two strided-pattern
+  sets, A_i = local_i | stride_i (the same merged integration of report
+  section 3.1, Eq. 7, applied to the strided pattern).
 * ``fixed_merged``: one head reads the union of the two fixed-pattern sets,
   A_i = same-block_i | summary_i (the merged integration of report section
   3.1, Eq. 7, which the Enwik8 model used; report section 4).  No row is
@@ -58,7 +61,8 @@ SAMEBLOCK = "sameblock"
 SUMMARY = "summary"
 FIXED_MERGED = "fixed_merged"
 LOCAL_GLOBAL = "local_global"
-KINDS = (LOCAL, STRIDE, SAMEBLOCK, SUMMARY, FIXED_MERGED, LOCAL_GLOBAL)
+STRIDED_MERGED = "strided_merged"
+KINDS = (LOCAL, STRIDE, SAMEBLOCK, SUMMARY, FIXED_MERGED, LOCAL_GLOBAL, STRIDED_MERGED)
 
 
 def summary_start(l: int, c: int, sub: int = 0) -> int:
@@ -100,6 +104,8 @@ def visible(kind: str, i, j, l: int, c: int | None = None, sub: int = 0):
         return causal & (r >= s) & (r <= s + c - 1)
     if kind == FIXED_MERGED:
         return visible(SAMEBLOCK, i, j, l) | visible(SUMMARY, i, j, l, c, sub)
+    if kind == STRIDED_MERGED:
+        return visible(LOCAL, i, j, l) | visible(STRIDE, i, j, l)
     if kind == LOCAL_GLOBAL:
         g = 0 if c is None else c  # None: no global tokens
         if g < 0:
@@ -150,6 +156,8 @@ def row_keys(kind: str, i: int, n: int, l: int, c: int | None = None,
     elif kind == FIXED_MERGED:
         keys = np.union1d(row_keys(SAMEBLOCK, i, n, l),
                           row_keys(SUMMARY, i, n, l, c, sub, self_if_empty=False))
+    elif kind == STRIDED_MERGED:
+        keys = np.union1d(row_keys(LOCAL, i, n, l), row_keys(STRIDE, i, n, l))
     elif kind == LOCAL_GLOBAL:
         g = 0 if c is None else c
         if g < 0:

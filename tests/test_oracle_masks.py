@@ -24,6 +24,8 @@ KINDS_SMALL = [
     (M.FIXED_MERGED, dict(l=6, c=1, sub=2)), (M.FIXED_MERGED, dict(l=5, c=5, sub=0)),
     (M.LOCAL_GLOBAL, dict(l=2, c=1)), (M.LOCAL_GLOBAL, dict(l=3, c=0)),
     (M.LOCAL_GLOBAL, dict(l=4, c=7)), (M.LOCAL_GLOBAL, dict(l=1, c=30)),
+    (M.STRIDED_MERGED, dict(l=1)), (M.STRIDED_MERGED, dict(l=3)), (M.STRIDED_MERGED, dict(l=8)),
+    (M.STRIDED_MERGED, dict(l=40)),
 ]
 
 
@@ -140,6 +142,31 @@ def test_fixed_merged_totals_and_special_cases():
     np.testing.assert_array_equal(m, np.tril(np.ones((40, 40), dtype=bool)))
 
 
+def test_strided_merged_worked_example(golden_dir):
+    """Report sections 2.2 and 3.1 (Eq. 7): a hand-worked 8-token merged strided head."""
+    meta, expect = _read_golden_matrix(os.path.join(golden_dir, "strided_merged_n8_l2.txt"))
+    n, l = meta["length"], meta["l"]
+    got = M.head_mask(n, M.STRIDED_MERGED, l)
+    np.testing.assert_array_equal(got, expect)
+    for i in range(n):
+        assert M.row_keys(M.STRIDED_MERGED, i, n, l).tolist() == np.flatnonzero(expect[i]).tolist()
+    assert got.sum() == 27
+    # The union covers every j <= i within one hop of the row itself or of a
+    # stride member (report section 2.1): with l = 1 it is dense causal.
+    np.testing.assert_array_equal(M.head_mask(30, M.STRIDED_MERGED, 1),
+                                  np.tril(np.ones((30, 30), dtype=bool)))
+
+
+def test_strided_merged_total_12288():
+    """Closed-form total of the merged strided head at n = 12,288, l = 128."""
+    n, l = 12288, 128
+    band = l * (l + 1) // 2 + (n - l) * (l + 1)
+    stride = l * (n // l) * (n // l + 1) // 2
+    overlap = n + (n - l)  # i itself, and i - l for i >= l
+    assert band + stride - overlap == 2148416
+    assert sum(M.row_keys(M.STRIDED_MERGED, i, n, l).size for i in range(n)) == 2148416
+
+
 def test_local_global_kind_is_the_worked_example(golden_dir):
     """Blog post section 04: window 2 plus global token 0 as the head kind (c = 1 leading token)."""
     meta, expect = _read_golden_matrix(os.path.join(golden_dir, "local_global_8x8.txt"))
@@ -178,6 +205,10 @@ def _closed_form_count(kind, i, l, c=None, s=None):
         # own block up to i, plus c cells of every earlier block (the cells of
         # the own block up to i are already in it)
         return i % l + 1 + (i // l) * c
+    if kind == M.STRIDED_MERGED:
+        # band min(i, l) + 1 keys, stride i // l + 1 keys; both hold i, and
+        # i - l as well once i >= l
+        return min(i, l) + i // l + 1 - (1 if i >= l else 0)
     if kind == M.LOCAL_GLOBAL:
         lo = max(0, i - l)
         return i - lo + 1 + min(c, lo)  # window, plus global tokens before it
