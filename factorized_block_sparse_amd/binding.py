@@ -21,7 +21,9 @@ LIB_NAME = "libsparse_attn.so"
 # enum values of sparse_attn.h
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ESIZE, SA_EHIP = 0, -1, -2, -3, -4
 KINDS = {"local": 0, "stride": 1, "sameblock": 2, "summary": 3, "fixed_merged": 4,
-         "local_global": 5}
+         "local_global": 5, "strided_merged": 6}
+SA_STRIDE_FAR = 7  # blob-only pattern kind: second part of a merged strided head
+PART_INIT = 1 << 30  # schedule pattern field: first chunk starts from the part state
 SA_BF16, SA_FP32 = 0, 1
 SA_SELF_IF_EMPTY = 1
 SA_BLOB_MAGIC = 0x31415053
@@ -76,7 +78,13 @@ class CBlobHeader(ctypes.Structure):
                 ("comb_sched_off", ctypes.c_int64), ("comb_sched_len", ctypes.c_int32),
                 ("num_qslots", ctypes.c_int32),
                 ("split_keys", ctypes.c_int32), ("split_rows", ctypes.c_int32),
-                ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64)]
+                ("pairs_all_heads", ctypes.c_int64), ("tiles_all_heads", ctypes.c_int64),
+                ("head_part_off", ctypes.c_int64), ("head_merged_off", ctypes.c_int64),
+                ("num_merged", ctypes.c_int32), ("fwdp_sched_len", ctypes.c_int32),
+                ("bwdp_sched_len", ctypes.c_int32), ("fwdp_xl_len", ctypes.c_int32),
+                ("bwdp_xl_len", ctypes.c_int32), ("pad0", ctypes.c_int32),
+                ("fwdp_sched_off", ctypes.c_int64), ("bwdp_sched_off", ctypes.c_int64),
+                ("fwdp_xitem_off", ctypes.c_int64), ("bwdp_xitem_off", ctypes.c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -145,8 +153,8 @@ def _check(rc: int, what: str):
 @dataclass(frozen=True)
 class HeadPattern:
     """One head's pattern: kind in {"local", "stride", "sameblock", "summary",
-    "fixed_merged", "local_global"}; c is the summary width, or for
-    "local_global" the number of leading global tokens."""
+    "fixed_merged", "local_global", "strided_merged"}; c is the summary width,
+    or for "local_global" the number of leading global tokens."""
     kind: str
     l: int
     c: int = 0
@@ -241,10 +249,27 @@ class Layout:
                          np.int32).reshape(-1, SA_SCHED_FIELDS)
 
     def xcd_items(self, which: str) -> np.ndarray:
-        """[SA_XCDS, len, SA_SCHED_FIELDS] schedule entries in list order ("fwd" or "bwd")."""
+        """[SA_XCDS, len, SA_SCHED_FIELDS] schedule entries in list order ("fwd", "bwd",
+        or "fwdp" / "bwdp" for the second parts of two-part heads)."""
         h = self.header
-        off, ln = (h.fwd_xitem_off, h.fwd_xl_len) if which == "fwd" else (h.bwd_xitem_off, h.bwd_xl_len)
+        off, ln = {"fwd": (h.fwd_xitem_off, h.fwd_xl_len), "bwd": (h.bwd_xitem_off, h.bwd_xl_len),
+                   "fwdp": (h.fwdp_xitem_off, h.fwdp_xl_len),
+                   "bwdp": (h.bwdp_xitem_off, h.bwdp_xl_len)}[which]
         return self._arr(off, SA_XCDS * ln * SA_SCHED_FIELDS, np.int32).reshape(SA_XCDS, ln, SA_SCHED_FIELDS)
+
+    def part_schedules(self) -> tuple:
+        """(forward, backward) schedules of the second parts of two-part heads, rows as
+        fwd_schedule (every tile holding a token, none split)."""
+        h = self.header
+        f = self._arr(h.fwdp_sched_off, SA_SCHED_FIELDS * h.fwdp_sched_len, np.int32)
+        b = self._arr(h.bwdp_sched_off, SA_SCHED_FIELDS * h.bwdp_sched_len, np.int32)
+        return f.reshape(-1, SA_SCHED_FIELDS), b.reshape(-1, SA_SCHED_FIELDS)
+
+    def head_parts(self) -> tuple:
+        """(second-part pattern index or -1, index among two-part heads or -1) per head."""
+        h = self.header
+        return (self._arr(h.head_part_off, h.num_heads, np.int32),
+                self._arr(h.head_merged_off, h.num_heads, np.int32))
 
     def xcd_lists(self, which: str) -> np.ndarray:
         """[SA_XCDS, len] schedule indices per XCD ("fwd" or "bwd"), -1 = padding."""

@@ -17,6 +17,8 @@ struct LaunchInfo {
   int64_t fwd_xl_off, bwd_xl_off, fwd_xitem_off, bwd_xitem_off;
   int32_t fwd_xl_len, bwd_xl_len;
   bool has_pre;  // some pattern's rows read a key prefix
+  int32_t num_merged, fwdp_xl_len, bwdp_xl_len;  // two-part heads and their part lists
+  int64_t fwdp_xitem_off, bwdp_xitem_off;
 };
 
 inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,6 +59,11 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   li->bwd_xl_len = h.bwd_xl_len;
   li->fwd_xitem_off = h.fwd_xitem_off;
   li->bwd_xitem_off = h.bwd_xitem_off;
+  li->num_merged = h.num_merged;
+  li->fwdp_xl_len = h.fwdp_xl_len;
+  li->bwdp_xl_len = h.bwdp_xl_len;
+  li->fwdp_xitem_off = h.fwdp_xitem_off;
+  li->bwdp_xitem_off = h.bwdp_xitem_off;
   li->has_pre = false;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

@@ -57,10 +57,53 @@ struct BwdParams {
   float* dsum;     // D, [B, H, n]
   float* partial;  // [B, num_slots, 2, BK, 64]: dK, dV chunks of split key tiles
   float* part_dq;  // [B, num_qslots, BQ, 64]: dQ chunks of split query tiles
+  // Two-part heads: float32 sums of every token after the second part,
+  // [B, num_merged, n, 64] each (dQ, dK, dV before the scale).  `part` != 0
+  // in the launches of the second parts, which write them; the main
+  // launches' first chunks read them.
+  float* st_dq;
+  float* st_dk;
+  float* st_dv;
+  int32_t num_merged, part;
   float scale;
   float scale_log2;
   PatTable pats;  // arrays of the first patterns (device addresses)
 };
+
+// Store the 64 features of a lane's row from two 32x32 accumulators (register
+// r of half g: feature 32*fb + kappa(r, g)) as float32, times `scale`.
+__device__ __forceinline__ void store_rows16(float* dst, const floatx16 (&acc)[2], int g, float scale) {
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      const int f0 = 32 * fb + 16 * h8 + 8 * g;
+      floatx4 x0, x1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x0[j] = acc[fb][8 * h8 + j] * scale;
+        x1[j] = acc[fb][8 * h8 + 4 + j] * scale;
+      }
+      *reinterpret_cast<floatx4*>(dst + f0) = x0;
+      *reinterpret_cast<floatx4*>(dst + f0 + 4) = x1;
+    }
+}
+
+// Load what store_rows16 stored (scale 1) into two accumulators.
+__device__ __forceinline__ void load_rows16(const float* src, floatx16 (&acc)[2], int g) {
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(src + 32 * fb + 16 * h8 + 8 * g);
+      const floatx4 c = *reinterpret_cast<const floatx4*>(src + 32 * fb + 16 * h8 + 8 * g + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[fb][8 * h8 + j] = a[j];
+        acc[fb][8 * h8 + 4 + j] = c[j];
+      }
+    }
+}
 
 // --------------------------------------------------------------------------
 // dQ pass: one workgroup per query tile, BQ = 32 * NW rows, key tiles of BK.
@@ -82,8 +125,8 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   int b;
   const int32_t* it8 = xcd_work_entry(p.qitems, p.qxl_len, p.B, &b);
   if (!it8) return;
-  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3], slot = it8[4];
-  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
+  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3], slot = it8[4], pf = it8[5];
+  const PatView pv = pattern_view(p.pats, p.blob, field_pattern(pf));
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int prow = qt * BQ + w * 32 + l32;
@@ -146,6 +189,9 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 
   floatx16 dqa[2];
   dqa[0] = dqa[1] = floatx16{};
+  // Register r of half g: feature 32*fb + kappa(r, g); lane = query row.
+  const size_t srow = (size_t(b) * p.num_merged + field_merged(pf)) * size_t(p.n) + size_t(tok);
+  if ((pf & kPartInit) && tok >= 0) load_rows16(p.st_dq + srow * kD, dqa, g);  // main part of a two-part head
   const float c2 = p.scale_log2;
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
@@ -220,7 +266,10 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     if (it + 1 < e1) key_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  // Register r of half g: feature 32*fb + kappa(r, g); lane = query row.
+  if (p.part) {  // second part of a two-part head: keep the sums
+    if (tok >= 0) store_rows16(p.st_dq + srow * kD, dqa, g, 1.f);
+    return;
+  }
   if (slot < 0) {
     if (tok >= 0) {
       bf16* row = p.dq + (base + tok) * kD;
@@ -285,8 +334,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   int b;
   const int32_t* it8 = xcd_work_entry(p.kitems, p.kxl_len, p.B, &b);
   if (!it8) return;
-  const int head = it8[0], kt = it8[1], c0 = it8[2], c1 = it8[3], slot = it8[4];
-  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
+  const int head = it8[0], kt = it8[1], c0 = it8[2], c1 = it8[3], slot = it8[4], pf = it8[5];
+  const PatView pv = pattern_view(p.pats, p.blob, field_pattern(pf));
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int kpos = kt * BK + 32 * w + l32;
@@ -310,6 +359,12 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
 
   floatx16 dva[2], dka[2];
   dva[0] = dva[1] = dka[0] = dka[1] = floatx16{};
+  // Register r of half g: feature 32*fb + kappa(r, g); lane = key.
+  const size_t srow = (size_t(b) * p.num_merged + field_merged(pf)) * size_t(p.n) + size_t(ktok);
+  if ((pf & kPartInit) && ktok >= 0) {  // main part of a two-part head
+    load_rows16(p.st_dk + srow * kD, dka, g);
+    load_rows16(p.st_dv + srow * kD, dva, g);
+  }
   const int nsteps = (c1 - c0) * NSTEP;
   const float c2 = p.scale_log2;
 
@@ -469,7 +524,13 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
     if (step + 1 < nsteps) q_step(std::integral_constant<int, 1>{}, step + 1);
   }
 
-  // Register r of half g: feature 32*fb + kappa(r, g); lane = key.
+  if (p.part) {  // second part of a two-part head: keep the sums
+    if (ktok >= 0) {
+      store_rows16(p.st_dk + srow * kD, dka, g, 1.f);
+      store_rows16(p.st_dv + srow * kD, dva, g, 1.f);
+    }
+    return;
+  }
   if (slot < 0) {
     if (ktok >= 0) {
       bf16* dkrow = p.dk + (base + ktok) * kD;
@@ -574,17 +635,23 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 // 64]] [dQ partials float32[B, query slots, BQ, 64]]; each part starts on a
 // 256-byte boundary.
 struct BwdWorkspace {
-  size_t dsum, partial, part_dq, total;
+  size_t dsum, partial, part_dq, st_dq, st_dk, st_dv, total;
 };
 
+// D, chunk partials of split key and query tiles, then the token sums of
+// two-part heads.
 BwdWorkspace bwd_workspace_layout(int B, int H, const sa_blob_header& h) {
   BwdWorkspace w{};
+  const size_t st = round256(size_t(B) * size_t(h.num_merged) * size_t(h.n) * sa::kD * sizeof(float));
   w.dsum = 0;
   w.partial = w.dsum + round256(size_t(B) * size_t(H) * size_t(h.n) * sizeof(float));
   w.part_dq = w.partial + round256(size_t(B) * size_t(h.num_slots) * 2 * size_t(h.block_k) *
                                    sa::kD * sizeof(float));
-  w.total = w.part_dq + round256(size_t(B) * size_t(h.num_qslots) * size_t(h.block_q) * sa::kD *
+  w.st_dq = w.part_dq + round256(size_t(B) * size_t(h.num_qslots) * size_t(h.block_q) * sa::kD *
                                  sizeof(float));
+  w.st_dk = w.st_dq + st;
+  w.st_dv = w.st_dk + st;
+  w.total = w.st_dv + st;
   return w;
 }
 
@@ -634,7 +701,10 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   const int64_t gk = int64_t(SA_XCDS) * li.bwd_xl_len * B;
   const int64_t gm = (int64_t(h.red_sched_len) * (2 * bk * kD / 2048) +
                       int64_t(h.comb_sched_len) * (bq * kD / 2048)) * B;
-  if (gq > INT32_MAX || gk > INT32_MAX || gm > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t gqp = int64_t(SA_XCDS) * li.fwdp_xl_len * B;
+  const int64_t gkp = int64_t(SA_XCDS) * li.bwdp_xl_len * B;
+  if (gq > INT32_MAX || gk > INT32_MAX || gm > INT32_MAX || gqp > INT32_MAX || gkp > INT32_MAX)
+    return SA_EUNSUPPORTED;
 
   BwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
@@ -664,6 +734,11 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   prm.dsum = reinterpret_cast<float*>(ws + wl.dsum);
   prm.partial = reinterpret_cast<float*>(ws + wl.partial);
   prm.part_dq = reinterpret_cast<float*>(ws + wl.part_dq);
+  prm.st_dq = reinterpret_cast<float*>(ws + wl.st_dq);
+  prm.st_dk = reinterpret_cast<float*>(ws + wl.st_dk);
+  prm.st_dv = reinterpret_cast<float*>(ws + wl.st_dv);
+  prm.num_merged = li.num_merged;
+  prm.part = 0;
   prm.scale = sc;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -678,6 +753,24 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     if (li.has_pre) SA_LAUNCH((KN<A, C, true>), g, threads); \
     else SA_LAUNCH((KN<A, C, false>), g, threads);      \
   } while (0)
+  // Second parts of two-part heads run first in each pass: they leave their
+  // sums of every token for the main launch.
+  BwdParams pp = prm;
+  pp.part = 1;
+  pp.qitems = reinterpret_cast<const int32_t*>(pp.blob + li.fwdp_xitem_off);
+  pp.kitems = reinterpret_cast<const int32_t*>(pp.blob + li.bwdp_xitem_off);
+  pp.qxl_len = li.fwdp_xl_len;
+  pp.kxl_len = li.bwdp_xl_len;
+#define SA_LAUNCH_PART(kern, grid, threads) \
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(threads), 0, st, pp)
+  if ((phases & SA_BWD_DQ) && gqp > 0) {
+    if (bq == 32 && bk == 32) SA_LAUNCH_PART((bwd_dq_kernel<32, 32, false>), gqp, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH_PART((bwd_dq_kernel<32, 64, false>), gqp, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH_PART((bwd_dq_kernel<64, 32, false>), gqp, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH_PART((bwd_dq_kernel<64, 64, false>), gqp, 128);
+    else if (bq == 128 && bk == 32) SA_LAUNCH_PART((bwd_dq_kernel<128, 32, false>), gqp, 256);
+    else SA_LAUNCH_PART((bwd_dq_kernel<128, 64, false>), gqp, 256);
+  }
   if ((phases & SA_BWD_DQ) && gq > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 32, 32, gq, 64);
     else if (bq == 32 && bk == 64) SA_LAUNCH_P(bwd_dq_kernel, 32, 64, gq, 64);
@@ -686,6 +779,15 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 128 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 128, 32, gq, 256);
     else SA_LAUNCH_P(bwd_dq_kernel, 128, 64, gq, 256);
   }
+  if ((phases & SA_BWD_DKDV) && gkp > 0) {
+    if (bq == 32 && bk == 32) SA_LAUNCH_PART((bwd_dkdv_kernel<32, 32, false>), gkp, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH_PART((bwd_dkdv_kernel<64, 32, false>), gkp, 64);
+    else if (bq == 128 && bk == 32) SA_LAUNCH_PART((bwd_dkdv_kernel<128, 32, false>), gkp, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH_PART((bwd_dkdv_kernel<32, 64, false>), gkp, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH_PART((bwd_dkdv_kernel<64, 64, false>), gkp, 128);
+    else SA_LAUNCH_PART((bwd_dkdv_kernel<128, 64, false>), gkp, 128);
+  }
+#undef SA_LAUNCH_PART
   if ((phases & SA_BWD_DKDV) && gk > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 32, 32, gk, 64);
     else if (bq == 64 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 64, 32, gk, 64);

@@ -253,6 +253,13 @@ __device__ __forceinline__ PatView pattern_view(const PatTable& t, const uint8_t
   return pi < kArgPatterns ? t.pv[pi] : pattern_of_index(blob, pi);
 }
 
+// Pattern field of a schedule entry: pattern index, (index among two-part
+// heads + 1) << 16, and kPartInit on the first chunk of such a head's tile
+// (it starts from the state the head's second part left in the workspace).
+constexpr int kPartInit = 1 << 30;
+__device__ __forceinline__ int field_pattern(int f) { return f & 0xffff; }
+__device__ __forceinline__ int field_merged(int f) { return ((f >> 16) & 0x3fff) - 1; }
+
 // A wave's register window over a tile list (CSR or CSC entries [e0, e1)):
 // lane l holds entry base + l packed as (tile << 1) | FULL, so the loop reads
 // an entry with one readlane instead of a global load whose latency would

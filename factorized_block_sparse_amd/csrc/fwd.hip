@@ -57,9 +57,18 @@ struct FwdParams {
   float* part_m;  // [B, num_qslots, BQ]: running max (base 2)
   float* part_l;  // [B, num_qslots, BQ]: running sum
   const int32_t* csched;  // (head, q-tile, first slot, chunks) of each split query tile
+  // Two-part heads: float32 softmax state of every token after the second
+  // part, [B, num_merged, n] rows (unnormalised O of 64 floats, running max
+  // base 2, running sum).  `part` != 0 in the launch of the second parts,
+  // which write it; the main launch's first chunks read it.
+  float* st_o;
+  float* st_m;
+  float* st_l;
+  int32_t num_merged, part;
   float scale_log2;  // softmax scale * log2(e)
   PatTable pats;     // arrays of the first patterns (device addresses)
 };
+
 
 // Merge of a split query tile (all chunks have stored their partials): per
 // row, m = max of the chunk maxima, O = sum_c 2^(m_c - m) acc_c / l with
@@ -172,8 +181,8 @@ void fwd_bf16_kernel(FwdParams p) {
   int b;
   const int32_t* it8 = xcd_work_entry(p.xitems, p.xl_len, p.B, &b);
   if (!it8) return;
-  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
-  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
+  const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3], pf = it8[5];
+  const PatView pv = pattern_view(p.pats, p.blob, field_pattern(pf));
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const bf16* qg = static_cast<const bf16*>(p.q) + base * kD;
   const bf16* kg = static_cast<const bf16*>(p.k) + base * kD;
@@ -224,6 +233,25 @@ void fwd_bf16_kernel(FwdParams p) {
   oacc[0] = floatx16{};
   oacc[1] = floatx16{};
   float m_run = kNegInit, l_run = 0.f;  // l_run: this half-wave's share of the row sum
+  // Main part of a two-part head: start from the second part's state.
+  const size_t srow = (size_t(b) * p.num_merged + field_merged(pf)) * size_t(p.n) + size_t(tok);
+  if ((pf & kPartInit) && tok >= 0) {
+    m_run = p.st_m[srow];
+    l_run = g == 0 ? p.st_l[srow] : 0.f;
+    const float* so = p.st_o + srow * kD;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(so + 32 * fb + 16 * h8 + 8 * g);
+        const floatx4 c = *reinterpret_cast<const floatx4*>(so + 32 * fb + 16 * h8 + 8 * g + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          oacc[fb][8 * h8 + j] = a[j];
+          oacc[fb][8 * h8 + 4 + j] = c[j];
+        }
+      }
+  }
   const float c2 = p.scale_log2;
 
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
@@ -320,7 +348,29 @@ void fwd_bf16_kernel(FwdParams p) {
     if (it + 1 < e1) tile_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
-  fwd_epilogue<bf16, BQ>(p, oacc, m_run, pair_sum(l_run), tok, base, b, it8[4], w * 32 + l32, g);
+  const float l_tot = pair_sum(l_run);
+  if (p.part) {
+    // Second part of a two-part head: keep the state for the main part.
+    if (tok >= 0) {
+      float* so = p.st_o + srow * kD;
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const int f0 = 32 * fb + 16 * h8 + 8 * g;
+          *reinterpret_cast<floatx4*>(so + f0) = floatx4{oacc[fb][8 * h8], oacc[fb][8 * h8 + 1],
+                                                         oacc[fb][8 * h8 + 2], oacc[fb][8 * h8 + 3]};
+          *reinterpret_cast<floatx4*>(so + f0 + 4) =
+              floatx4{oacc[fb][8 * h8 + 4], oacc[fb][8 * h8 + 5], oacc[fb][8 * h8 + 6], oacc[fb][8 * h8 + 7]};
+        }
+      if (g == 0) {
+        p.st_m[srow] = m_run;
+        p.st_l[srow] = l_tot;
+      }
+    }
+    return;
+  }
+  fwd_epilogue<bf16, BQ>(p, oacc, m_run, l_tot, tok, base, b, it8[4], w * 32 + l32, g);
 }
 
 // --------------------------------------------------------------------------
@@ -344,7 +394,7 @@ __global__ __launch_bounds__(BQ * 2) void fwd_f32_kernel(FwdParams p) {
   const int32_t* it8 = xcd_work_entry(p.xitems, p.xl_len, p.B, &b);
   if (!it8) return;
   const int head = it8[0], qt = it8[1], e0 = it8[2], e1 = it8[3];
-  const PatView pv = pattern_view(p.pats, p.blob, it8[5]);
+  const PatView pv = pattern_view(p.pats, p.blob, field_pattern(it8[5]));
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
   const float* qg = static_cast<const float*>(p.q) + base * kD;
   const float* kg = static_cast<const float*>(p.k) + base * kD;
@@ -494,17 +544,22 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 // slots, BQ]] [partial sum, same]; each part starts on a 256-byte boundary.
 // Empty when no query tile is split.
 struct FwdWorkspace {
-  size_t part_o, part_m, part_l, total;
+  size_t part_o, part_m, part_l, st_o, st_m, st_l, total;
 };
 
+// Chunk partials of split query tiles, then the token state of two-part heads.
 FwdWorkspace fwd_workspace_layout(int B, const sa_blob_header& h) {
   FwdWorkspace w{};
-  if (h.num_qslots == 0 || B == 0) return w;
+  if (B == 0) return w;
   const size_t rows = size_t(B) * size_t(h.num_qslots) * size_t(h.block_q);
+  const size_t srows = size_t(B) * size_t(h.num_merged) * size_t(h.n);
   w.part_o = 0;
   w.part_m = w.part_o + round256(rows * sa::kD * sizeof(float));
   w.part_l = w.part_m + round256(rows * sizeof(float));
-  w.total = w.part_l + round256(rows * sizeof(float));
+  w.st_o = w.part_l + round256(rows * sizeof(float));
+  w.st_m = w.st_o + round256(srows * sa::kD * sizeof(float));
+  w.st_l = w.st_m + round256(srows * sizeof(float));
+  w.total = w.st_l + round256(srows * sizeof(float));
   return w;
 }
 
@@ -542,6 +597,7 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
   const int bq = li.block_q, bk = li.block_k;
   const bool shape_ok = dtype == SA_BF16 ? (bk == 32 || bk == 64) : (bk == 32);
   if (!shape_ok) return SA_EUNSUPPORTED;
+  if (dtype != SA_BF16 && li.num_merged > 0) return SA_EUNSUPPORTED;  // two-part heads: bf16 only
   if (B == 0 || li.fwd_xl_len == 0) return SA_OK;  // empty batch: pointers may be NULL
   const FwdWorkspace wl = fwd_workspace_layout(B, h);
   if (ws_bytes < wl.total) return SA_ESIZE;
@@ -550,7 +606,8 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
     return SA_EINVAL;
   const int64_t grid = int64_t(SA_XCDS) * li.fwd_xl_len * B;
   const int64_t mgrid = int64_t(h.comb_sched_len) * (bq / 32) * B;
-  if (grid > INT32_MAX || mgrid > INT32_MAX) return SA_EUNSUPPORTED;
+  const int64_t pgrid = int64_t(SA_XCDS) * li.fwdp_xl_len * B;
+  if (grid > INT32_MAX || mgrid > INT32_MAX || pgrid > INT32_MAX) return SA_EUNSUPPORTED;
 
   FwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
@@ -572,6 +629,11 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
   prm.part_o = split ? reinterpret_cast<float*>(ws + wl.part_o) : nullptr;
   prm.part_m = split ? reinterpret_cast<float*>(ws + wl.part_m) : nullptr;
   prm.part_l = split ? reinterpret_cast<float*>(ws + wl.part_l) : nullptr;
+  prm.st_o = split ? reinterpret_cast<float*>(ws + wl.st_o) : nullptr;
+  prm.st_m = split ? reinterpret_cast<float*>(ws + wl.st_m) : nullptr;
+  prm.st_l = split ? reinterpret_cast<float*>(ws + wl.st_l) : nullptr;
+  prm.num_merged = li.num_merged;
+  prm.part = 0;
   prm.scale_log2 = float(double(sc) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -584,6 +646,24 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
     if (li.has_pre) SA_LAUNCH((KN<A, C, true>), g, threads); \
     else SA_LAUNCH((KN<A, C, false>), g, threads);      \
   } while (0)
+  if ((phases & SA_FWD_MAIN) && pgrid > 0) {
+    // Second parts of two-part heads first: they leave the softmax state of
+    // every token for the main launch.
+    FwdParams pp = prm;
+    pp.part = 1;
+    pp.xitems = reinterpret_cast<const int32_t*>(pp.blob + li.fwdp_xitem_off);
+    pp.xl_len = li.fwdp_xl_len;
+#define SA_LAUNCH_PART(BQv, BKv, threads)                                                        \
+  hipLaunchKernelGGL((fwd_bf16_kernel<BQv, BKv, false>), dim3(unsigned(pgrid)), dim3(threads), 0, \
+                     st, pp)
+    if (bq == 32 && bk == 32) SA_LAUNCH_PART(32, 32, 64);
+    else if (bq == 32 && bk == 64) SA_LAUNCH_PART(32, 64, 64);
+    else if (bq == 64 && bk == 32) SA_LAUNCH_PART(64, 32, 128);
+    else if (bq == 64 && bk == 64) SA_LAUNCH_PART(64, 64, 128);
+    else if (bq == 128 && bk == 32) SA_LAUNCH_PART(128, 32, 256);
+    else SA_LAUNCH_PART(128, 64, 256);
+#undef SA_LAUNCH_PART
+  }
   if (phases & SA_FWD_MAIN) {
     if (dtype == SA_BF16) {
       if (bq == 32 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 32, 32, grid, 64);

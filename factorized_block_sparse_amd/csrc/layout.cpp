@@ -23,7 +23,13 @@
 //           a prefix; the other tokens follow in order, so the rest of its
 //           block up to itself is an interval;
 //   local + global tokens (blog post sections 03, 04): identity order, the
-//           global tokens before the window as the prefix.
+//           global tokens before the window as the prefix;
+//   merged strided (report section 3.1, Eq. 7, on the strided pattern): no
+//           single order makes both its sets intervals, so the head runs as
+//           two parts with disjoint key sets -- its local band (a local
+//           pattern) and the stride members at distance >= 2l (residue-class
+//           order, the row's class up to two positions before itself) --
+//           whose results are combined per token by the kernels.
 // The prefix is empty for the first four kinds.  This is what makes tiles
 // dense for the stride and summary heads instead of holding one useful key
 // per row.
@@ -70,7 +76,7 @@ sa_head_pattern canonical(const sa_head_pattern& h) {
 }
 
 int check_head(const sa_head_pattern& h) {
-  if (h.kind < SA_LOCAL || h.kind > SA_LOCAL_GLOBAL) return SA_EINVAL;
+  if (h.kind < SA_LOCAL || h.kind > SA_STRIDED_MERGED) return SA_EINVAL;
   if (h.l < 1) return SA_EINVAL;
   if (has_summary(h.kind)) {
     if (h.c < 1 || h.c > h.l || h.sub < 0) return SA_EINVAL;
@@ -103,8 +109,12 @@ int build_maps(Pattern& P, int64_t n64, int32_t n_pad, bool self_if_empty) {
         P.hi[i] = i;
       }
       break;
-    case SA_STRIDE: {
+    case SA_STRIDE:
+    case SA_STRIDE_FAR: {
       // Residue r holds ceil((n - r) / l) tokens; classes are laid out in order.
+      // The far variant stops two positions short (distance >= 2l); its rows
+      // t < 2 read nothing.
+      const int32_t skip = P.p.kind == SA_STRIDE_FAR ? 2 : 0;
       const int32_t classes = int32_t(std::min<int64_t>(l, n));
       std::vector<int32_t> off(classes + 1, 0);
       for (int32_t r = 0; r < classes; ++r) off[r + 1] = off[r] + (n - r + l - 1) / l;
@@ -112,8 +122,10 @@ int build_maps(Pattern& P, int64_t n64, int32_t n_pad, bool self_if_empty) {
         const int32_t r = i % l, t = i / l;
         const int32_t p = off[r] + t;
         P.qmap[p] = P.kmap[p] = i;
-        P.lo[p] = off[r];
-        P.hi[p] = p;
+        if (t >= skip) {
+          P.lo[p] = off[r];
+          P.hi[p] = p - skip;
+        }
       }
       break;
     }
@@ -366,11 +378,11 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
 
   std::vector<Pattern> pats;
   std::map<std::tuple<int32_t, int32_t, int32_t, int32_t>, int32_t> index;
-  std::vector<int32_t> head_pat(desc->num_heads);
-  for (int32_t h = 0; h < desc->num_heads; ++h) {
-    const int rc = check_head(desc->heads[h]);
-    if (rc != SA_OK) return rc;
-    const sa_head_pattern c = canonical(desc->heads[h]);
+  std::vector<int32_t> head_pat(desc->num_heads), head_part(desc->num_heads, -1);
+  std::vector<int32_t> head_merged(desc->num_heads, -1);
+  int32_t num_merged = 0;
+  // Index of pattern c, built on first use (negative: an error status).
+  auto pattern_index = [&](const sa_head_pattern& c) -> int32_t {
     const auto key = std::make_tuple(c.kind, c.l, c.c, c.sub);
     auto it = index.find(key);
     if (it == index.end()) {
@@ -382,8 +394,27 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       it = index.emplace(key, int32_t(pats.size())).first;
       pats.push_back(std::move(P));
     }
-    head_pat[h] = it->second;
+    return it->second;
+  };
+  for (int32_t h = 0; h < desc->num_heads; ++h) {
+    const int rc = check_head(desc->heads[h]);
+    if (rc != SA_OK) return rc;
+    const sa_head_pattern c = canonical(desc->heads[h]);
+    if (c.kind == SA_STRIDED_MERGED) {
+      const int32_t a = pattern_index(sa_head_pattern{SA_LOCAL, c.l, 0, 0});
+      const int32_t f = pattern_index(sa_head_pattern{SA_STRIDE_FAR, c.l, 0, 0});
+      if (a < 0) return a;
+      if (f < 0) return f;
+      head_pat[h] = a;
+      head_part[h] = f;
+      head_merged[h] = num_merged++;
+    } else {
+      const int32_t a = pattern_index(c);
+      if (a < 0) return a;
+      head_pat[h] = a;
+    }
   }
+  if (pats.size() > 0xffff || num_merged > 0x3ffe) return SA_EUNSUPPORTED;
 
   std::vector<SchedItem> fwd_items, bwd_items;
   std::vector<int32_t> red_sched;   // (head, k-tile, first slot, chunks)
@@ -398,6 +429,10 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     const Pattern& P = pats[head_pat[h]];
     pairs_all += P.pairs;
     tiles_all += int64_t(P.col.size());
+    if (head_part[h] >= 0) {
+      pairs_all += pats[head_part[h]].pairs;
+      tiles_all += int64_t(pats[head_part[h]].col.size());
+    }
     for (int32_t qt = 0; qt < nqt; ++qt) {
       const int32_t r0 = P.row_ptr[qt], r1 = P.row_ptr[qt + 1], len = r1 - r0;
       if (len == 0) continue;
@@ -448,13 +483,46 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       num_slots += chunks;
     }
   }
-  for (auto& it : fwd_items) it.pattern = head_pat[it.head];
-  for (auto& it : bwd_items) it.pattern = head_pat[it.head];
+  // Pattern field: pattern index, (two-part head index + 1) << 16, and
+  // kPartInit on the first chunk of each of a two-part head's tiles.
+  constexpr int32_t kPartInit = int32_t(1) << 30;
+  auto pattern_field = [&](int32_t h, int32_t pat, bool first) {
+    int32_t f = pat;
+    if (head_merged[h] >= 0) f |= ((head_merged[h] + 1) << 16) | (first ? kPartInit : 0);
+    return f;
+  };
+  for (auto& it : fwd_items) it.pattern = pattern_field(it.head, head_pat[it.head], it.slot == it.slot0);
+  for (auto& it : bwd_items) it.pattern = pattern_field(it.head, head_pat[it.head], it.slot == it.slot0);
+  // Second parts: every tile holding a token, none split.
+  std::vector<SchedItem> fwdp_items, bwdp_items;
+  for (int32_t h = 0; h < desc->num_heads; ++h) {
+    if (head_part[h] < 0) continue;
+    const Pattern& P = pats[head_part[h]];
+    const int32_t f = pattern_field(h, head_part[h], false);
+    for (int32_t qt = 0; qt < nqt && qt * bq < n; ++qt) {
+      SchedItem it{h, qt, P.row_ptr[qt + 1] - P.row_ptr[qt] + 1};
+      it.e0 = P.row_ptr[qt];
+      it.e1 = P.row_ptr[qt + 1];
+      it.pattern = f;
+      fwdp_items.push_back(it);
+    }
+    for (int32_t kt = 0; kt < nkt && kt * bk < n; ++kt) {
+      SchedItem it{h, kt, P.col_ptr[kt + 1] - P.col_ptr[kt] + 1};
+      it.e0 = P.col_ptr[kt];
+      it.e1 = P.col_ptr[kt + 1];
+      it.pattern = f;
+      bwdp_items.push_back(it);
+    }
+  }
   const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
-  std::vector<int32_t> fwd_xl, bwd_xl;
+  const std::vector<int32_t> fwdp_sched = sorted_schedule(fwdp_items);
+  const std::vector<int32_t> bwdp_sched = sorted_schedule(bwdp_items);
+  std::vector<int32_t> fwd_xl, bwd_xl, fwdp_xl, bwdp_xl;
   const int32_t fwd_xl_len = xcd_lists(fwd_items, fwd_xl);
   const int32_t bwd_xl_len = xcd_lists(bwd_items, bwd_xl);
+  const int32_t fwdp_xl_len = fwdp_items.empty() ? 0 : xcd_lists(fwdp_items, fwdp_xl);
+  const int32_t bwdp_xl_len = bwdp_items.empty() ? 0 : xcd_lists(bwdp_items, bwdp_xl);
   // The entries in list order (padding: all -1).
   auto list_items = [](const std::vector<int32_t>& xl, const std::vector<int32_t>& sched) {
     std::vector<int32_t> out;
@@ -466,6 +534,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   };
   const std::vector<int32_t> fwd_xitem = list_items(fwd_xl, fwd_sched);
   const std::vector<int32_t> bwd_xitem = list_items(bwd_xl, bwd_sched);
+  const std::vector<int32_t> fwdp_xitem = list_items(fwdp_xl, fwdp_sched);
+  const std::vector<int32_t> bwdp_xitem = list_items(bwdp_xl, bwdp_sched);
 
   // Two passes: size, then write.
   for (int pass = 0; pass < 2; ++pass) {
@@ -484,6 +554,12 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwd_xl_off = w.put(bwd_xl);
     hdr.fwd_xitem_off = w.put(fwd_xitem);
     hdr.bwd_xitem_off = w.put(bwd_xitem);
+    hdr.head_part_off = w.put(head_part);
+    hdr.head_merged_off = w.put(head_merged);
+    hdr.fwdp_sched_off = w.put(fwdp_sched);
+    hdr.bwdp_sched_off = w.put(bwdp_sched);
+    hdr.fwdp_xitem_off = w.put(fwdp_xitem);
+    hdr.bwdp_xitem_off = w.put(bwdp_xitem);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
       sa_pattern_rec& r = recs[i];
@@ -545,6 +621,11 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwd_xl_len = bwd_xl_len;
     hdr.pairs_all_heads = pairs_all;
     hdr.tiles_all_heads = tiles_all;
+    hdr.num_merged = num_merged;
+    hdr.fwdp_sched_len = int32_t(fwdp_items.size());
+    hdr.bwdp_sched_len = int32_t(bwdp_items.size());
+    hdr.fwdp_xl_len = fwdp_xl_len;
+    hdr.bwdp_xl_len = bwdp_xl_len;
     std::memcpy(blob + hdr_at, &hdr, sizeof(hdr));
     std::memcpy(blob + rec_at, recs.data(), recs.size() * sizeof(sa_pattern_rec));
     *blob_bytes = size_t(total);
@@ -575,8 +656,9 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
   const int64_t total = h.total_bytes;
   if (total < int64_t(sizeof(h)) || size_t(total) > blob_bytes) return SA_ESIZE;
   if (h.n < 1 || h.n > kMaxN || !valid_tile(h.block_q) || !valid_tile(h.block_k)) return SA_EINVAL;
+  // At most two patterns per head (the parts of a merged strided head).
   if (h.num_heads < 1 || h.num_heads > kMaxHeads || h.num_patterns < 1 ||
-      h.num_patterns > h.num_heads)
+      h.num_patterns > 2 * h.num_heads)
     return SA_EINVAL;
   const int64_t t = std::max(h.block_q, h.block_k);
   if (h.n_pad != ((h.n + t - 1) / t) * t || h.nqt * h.block_q != h.n_pad ||
@@ -591,7 +673,15 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
       !in_blob(h.fwd_xl_off, 4 * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
       !in_blob(h.bwd_xl_off, 4 * int64_t(SA_XCDS) * h.bwd_xl_len, total) ||
       !in_blob(h.fwd_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.fwd_xl_len, total) ||
-      !in_blob(h.bwd_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwd_xl_len, total))
+      !in_blob(h.bwd_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwd_xl_len, total) ||
+      !in_blob(h.head_part_off, 4 * int64_t(h.num_heads), total) ||
+      !in_blob(h.head_merged_off, 4 * int64_t(h.num_heads), total) || h.num_merged < 0 ||
+      h.num_merged > h.num_heads || h.fwdp_sched_len < 0 || h.bwdp_sched_len < 0 ||
+      h.fwdp_xl_len < 0 || h.bwdp_xl_len < 0 ||
+      !in_blob(h.fwdp_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.fwdp_sched_len), total) ||
+      !in_blob(h.bwdp_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.bwdp_sched_len), total) ||
+      !in_blob(h.fwdp_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.fwdp_xl_len, total) ||
+      !in_blob(h.bwdp_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwdp_xl_len, total))
     return SA_EINVAL;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;
@@ -609,9 +699,12 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
       return SA_EINVAL;
   }
   for (int32_t hh = 0; hh < h.num_heads; ++hh) {
-    int32_t p;
+    int32_t p, q, m;
     std::memcpy(&p, b + h.head_pattern_off + 4 * hh, 4);
-    if (p < 0 || p >= h.num_patterns) return SA_EINVAL;
+    std::memcpy(&q, b + h.head_part_off + 4 * hh, 4);
+    std::memcpy(&m, b + h.head_merged_off + 4 * hh, 4);
+    if (p < 0 || p >= h.num_patterns || q < -1 || q >= h.num_patterns) return SA_EINVAL;
+    if ((q < 0) != (m < 0) || m >= h.num_merged) return SA_EINVAL;
   }
   return SA_OK;
 }

@@ -31,6 +31,7 @@ import torch
 
 LOCAL = "local"
 STRIDE = "stride"
+STRIDED_MERGED = "strided_merged"
 SAMEBLOCK = "sameblock"
 SUMMARY = "summary"
 FIXED_MERGED = "fixed_merged"
@@ -101,6 +102,11 @@ WORKLOADS = {
         Workload("local_global_n12288", 2, 8, 12288, 64,
                  tuple(HeadSpec(LOCAL_GLOBAL, 256, 64) for _ in range(8)), "bf16", 64, 64, 1008,
                  note="causal window of 256 plus 64 leading global tokens (blog post sections 03-04)"),
+        Workload("strided_merged_n12288", 1, 16, 12288, 64,
+                 tuple(HeadSpec(STRIDED_MERGED, 128) for _ in range(16)), "bf16", 32, 32, 1009,
+                 sinusoid=True,
+                 note="merged strided heads (local band and stride in one head, l=128) at "
+                      "12,288 with the shared period-128 sinusoid in Q and K"),
         Workload("strided_n65536", 1, 8, 65536, 64, strided_heads(8, 256), "bf16", 64, 64, 1005,
                  note="long strided pattern at the audio length 65,536"),
     )

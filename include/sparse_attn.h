@@ -18,6 +18,11 @@
  *     SA_LOCAL_GLOBAL  {j <= i : i - j <= l or j < c}: the causal window plus
  *                   the first c positions as global tokens (blog post sections
  *                   03 and 04)
+ *     SA_STRIDED_MERGED  one head reading the union of the two strided sets
+ *                   (report section 3.1, Eq. 7), run in two parts with
+ *                   disjoint key sets: the stride members at distance >= 2l
+ *                   first, then the local band, which starts from the first
+ *                   part's softmax state (forward) or sums (backward)
  * Rows left empty by a summary head (i < s) read only themselves when
  * SA_SELF_IF_EMPTY is set (the default reading; without it such a layout is
  * rejected, since an empty row has no softmax).  Execution is at tile
@@ -71,7 +76,11 @@ enum sa_head_kind {
   SA_SAMEBLOCK = 2,
   SA_SUMMARY = 3,
   SA_FIXED_MERGED = 4,
-  SA_LOCAL_GLOBAL = 5
+  SA_LOCAL_GLOBAL = 5,
+  SA_STRIDED_MERGED = 6,
+  /* blob-only pattern kind (never a head's kind): {j <= i : i - j >= 2l,
+   * (i - j) mod l == 0}, the second part of an SA_STRIDED_MERGED head */
+  SA_STRIDE_FAR = 7
 };
 
 enum sa_dtype { SA_BF16 = 0, SA_FP32 = 1 };
@@ -120,6 +129,8 @@ typedef struct {
  *   SA_FIXED_MERGED: queries identity; keys are the summary cells in
  *     increasing order, then every other token in increasing order.
  *   SA_LOCAL_GLOBAL: identity.
+ *   SA_STRIDE_FAR: residue-class order as SA_STRIDE; a row reads its own class
+ *     up to two positions before itself.
  * In layout space every query row reads a prefix and one interval of key
  * positions, [0, pre[p]) and [lo[p], hi[p]], with pre[p] <= lo[p] when the
  * interval is not empty (lo > hi: empty).  The prefix is empty except for
@@ -134,7 +145,7 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 8u
+#define SA_BLOB_VERSION 9u
 #define SA_SCHED_FIELDS 8
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
@@ -211,6 +222,26 @@ typedef struct {
   int32_t split_keys, split_rows; /* chunk caps the schedules were built with */
   int64_t pairs_all_heads;  /* sum of pairs over the heads (one batch element) */
   int64_t tiles_all_heads;  /* sum of active tiles over the heads */
+  /* Two-part heads (SA_STRIDED_MERGED).  The head's first pattern (head
+   * pattern table) is its local band; its second part is listed here and runs
+   * in separate launches before the main ones, writing float32 state per
+   * token (forward: unnormalised O, running max, row sum; backward: dQ, dK,
+   * dV sums) into the workspace; the main launches' first chunk of each of
+   * the head's tiles starts from it.  Schedule entries of two-part heads
+   * carry (index among them + 1) << 16 in the pattern field, and main
+   * entries that start from the state also 1 << 30; the pattern index is
+   * the low 16 bits. */
+  int64_t head_part_off;    /* int32[num_heads]: second-part pattern, -1 if none */
+  int64_t head_merged_off;  /* int32[num_heads]: index among two-part heads, -1 */
+  int32_t num_merged;       /* two-part heads */
+  int32_t fwdp_sched_len, bwdp_sched_len;
+  int32_t fwdp_xl_len, bwdp_xl_len;
+  int32_t pad0;
+  int64_t fwdp_sched_off;   /* int32[SA_SCHED_FIELDS * fwdp_sched_len]: second-part q-tiles
+                               (every one, none split) */
+  int64_t bwdp_sched_off;   /* the same over second-part k-tiles */
+  int64_t fwdp_xitem_off;   /* int32[SA_XCDS * fwdp_xl_len * SA_SCHED_FIELDS], as fwd_xitem */
+  int64_t bwdp_xitem_off;   /* int32[SA_XCDS * bwdp_xl_len * SA_SCHED_FIELDS] */
 } sa_blob_header;
 
 /* Build the layout.  With blob == NULL, only *blob_bytes is set (size query).
@@ -234,7 +265,9 @@ int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes);
  * stream). */
 
 /* Bytes of device workspace sparse_attn_fwd needs for these sizes (0 when
- * the layout splits no query tile; the workspace may then be NULL). */
+ * the layout splits no query tile and has no two-part head; the workspace
+ * may then be NULL).  Two-part heads add float32 state of every token:
+ * B * (two-part heads) * n * (64 + 2) floats. */
 int sparse_attn_fwd_workspace(const void* blob_host, int B, int H, int d, int dtype,
                               size_t* bytes);
 
@@ -246,9 +279,10 @@ int sparse_attn_fwd(const void* blob_host, const void* blob_dev, int B, int H, i
                     void* workspace, size_t ws_bytes, float scale, void* stream);
 
 /* The forward's two launches, separately (same arguments, one stream, in
- * order): SA_FWD_MAIN runs the block-sparse kernel (unsplit query tiles
- * write O and LSE, chunks of split tiles write partial results to the
- * workspace); SA_FWD_MERGE merges the chunks of split tiles (the running
+ * order): SA_FWD_MAIN runs the block-sparse kernel (second parts of two-part
+ * heads first, in a launch of their own; then unsplit query tiles write O
+ * and LSE, chunks of split tiles write partial results to the workspace);
+ * SA_FWD_MERGE merges the chunks of split tiles (the running
  * maxima rescaled to their common maximum) and writes their O and LSE.
  * sparse_attn_fwd runs SA_FWD_ALL. */
 enum { SA_FWD_MAIN = 1, SA_FWD_MERGE = 2, SA_FWD_ALL = 3 };
@@ -264,7 +298,8 @@ int sparse_attn_bwd_workspace(const void* blob_host, int B, int H, int d, int dt
 /* Backward by recomputation from LSE (report section 3.4): gradients of
  * sum(O * dO) with respect to q, k, v, written in dtype.  `o` and `lse` must
  * be the forward's outputs for the same inputs and scale.  Keys no query
- * reads in a head get exact zeros.  Only SA_BF16. */
+ * reads in a head get exact zeros.  Only SA_BF16.  Two-part heads add three
+ * float32 [B, two-part heads, n, 64] sums to the workspace. */
 int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, int d, int dtype,
                     const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
@@ -274,9 +309,11 @@ int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, i
  * other work between them or time them one by one:
  *   SA_BWD_DQ     per query tile (long tiles in chunks): D_i = dO_i . O_i
  *                 (kept in the workspace) and dQ, or float32 partial dQ of
- *                 split tiles (workspace);
+ *                 split tiles (workspace); second parts of two-part heads
+ *                 first, in a launch of their own;
  *   SA_BWD_DKDV   per key tile (long tiles in chunks): dK and dV, or float32
- *                 partial sums of split tiles (workspace);
+ *                 partial sums of split tiles (workspace); second parts
+ *                 first, likewise;
  *   SA_BWD_MERGE  sums the partials of split query and key tiles in a fixed
  *                 order and writes their dQ, dK, dV.
  * Phases must run in this order on one stream with the same arguments and

@@ -57,6 +57,20 @@ SMALL = [
                                                HeadPattern("local_global", 1, 1000)]),
     ("split_merged_global", 1, 2300, 64, 64, [HeadPattern("fixed_merged", 128, 32, 2),
                                               HeadPattern("local_global", 256, 300)], 512),
+    # merged strided heads: stride part first, band part starting from its state
+    ("strided_merged_tiles64", 2, 700, 64, 64, [HeadPattern("strided_merged", 32),
+                                                HeadPattern("local", 32),
+                                                HeadPattern("strided_merged", 24),
+                                                HeadPattern("summary", 64, 16, 1)]),
+    ("strided_merged_ragged", 1, 333, 64, 32, [HeadPattern("strided_merged", 7),
+                                               HeadPattern("strided_merged", 1),
+                                               HeadPattern("stride", 7),
+                                               HeadPattern("strided_merged", 500)]),
+    ("strided_merged_tiles32", 1, 300, 32, 32, [HeadPattern("strided_merged", 10),
+                                                HeadPattern("fixed_merged", 20, 4, 1)]),
+    ("strided_merged_q128_k64", 1, 640, 128, 64, [HeadPattern("strided_merged", 40)]),
+    ("split_strided_merged", 1, 2300, 64, 64, [HeadPattern("strided_merged", 1100),
+                                               HeadPattern("strided_merged", 16)], 512),
 ]
 
 
@@ -206,7 +220,8 @@ def _sample_rows(n, l, rng, extra=6):
 
 
 @pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "fixed_c8_n12288", "strided_n65536",
-                                   "fixed_merged_n12288", "local_global_n12288"])
+                                   "fixed_merged_n12288", "local_global_n12288",
+                                   "strided_merged_n12288"])
 def test_workload_full_size_sampled(wname):
     w = W.WORKLOADS[wname]
     lay = Layout(w.n, w.heads, w.block_q, w.block_k)

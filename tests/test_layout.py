@@ -493,3 +493,84 @@ def test_profile_summaries_parse_and_track_the_sources(tmp_path):
     stale.write_text(open(path).read().replace(recorded, "0" * 64))
     rec2, _ = profiling.read_traffic(str(stale))
     assert rec2 != profiling.source_hash()
+
+
+@pytest.mark.parametrize("n,bq,bk,l", [(300, 64, 32, 7), (1024, 32, 32, 32), (700, 128, 64, 24),
+                                       (97, 32, 64, 10), (40, 64, 64, 1), (130, 64, 64, 500)])
+def test_strided_merged_parts_are_disjoint_layouts_of_the_union(n, bq, bk, l):
+    """A merged strided head runs as its local band (a local pattern) plus the
+    stride members at distance >= 2l (residue-class order): disjoint, their
+    union is the oracle's merged set, each part bit-exact like any pattern."""
+    heads = [HeadPattern("strided_merged", l), HeadPattern("local", l), HeadPattern("strided_merged", l)]
+    lay = Layout(n, heads, bq, bk)
+    h = lay.header
+    t = max(bq, bk)
+    n_pad = -(-n // t) * t
+    hp = lay.head_pattern_index()
+    part, merged = lay.head_parts()
+    assert part.tolist()[1] == -1 and merged.tolist() == [0, -1, 1] and h.num_merged == 2
+    assert hp[0] == hp[1] == hp[2] and part[0] == part[2]  # shared band and part patterns
+    band = M.head_mask(n, M.LOCAL, l)
+    far = M.head_mask(n, M.STRIDE, l) & ~band
+    np.testing.assert_array_equal(band | far, M.head_mask(n, M.STRIDED_MERGED, l))
+    rec = lay.pattern_rec(int(part[0]))
+    assert (rec.kind, rec.l, rec.pre_off) == (bd.SA_STRIDE_FAR, l, 0)
+    arr = lay.pattern_arrays(int(part[0]))
+    qmap, kmap = _doc_maps("stride", n, n_pad, l)
+    np.testing.assert_array_equal(arr["qmap"], qmap)
+    np.testing.assert_array_equal(arr["kmap"], kmap)
+    mp = np.zeros((n_pad, n_pad), dtype=bool)
+    mp[:n, :n] = far[np.ix_(qmap[:n], kmap[:n])]
+    cols = np.arange(n_pad)
+    interval = (cols[None, :] >= arr["lo"][:, None]) & (cols[None, :] <= arr["hi"][:, None])
+    np.testing.assert_array_equal(interval, mp)
+    np.testing.assert_array_equal(arr["count"], far.sum(1))
+    assert rec.pairs == far.sum()
+    ref = _ref_tiles(mp, bq, bk)
+    for name, r in zip(("row_ptr", "col", "fflag", "col_ptr", "row", "bflag"), ref):
+        np.testing.assert_array_equal(arr[name], r, err_msg=name)
+    assert lay.pairs_per_batch() == 2 * int(band.sum() + far.sum()) + int(band.sum())
+    # Second-part schedules: every tile holding a token, unsplit, in the part's lists.
+    fp, bp = lay.part_schedules()
+    nq = [q for q in range(h.nqt) if q * bq < n]
+    nk = [k for k in range(h.nkt) if k * bk < n]
+    assert sorted((int(r[0]), int(r[1])) for r in fp) == [(hh, q) for hh in (0, 2) for q in nq]
+    assert sorted((int(r[0]), int(r[1])) for r in bp) == [(hh, k) for hh in (0, 2) for k in nk]
+    for sched, ptr in ((fp, arr["row_ptr"]), (bp, arr["col_ptr"])):
+        for head, tile, e0, e1, slot, pf, slot0, nch in sched.tolist():
+            assert (e0, e1, slot, slot0, nch) == (ptr[tile], ptr[tile + 1], -1, -1, 1)
+            assert pf == int(part[0]) | ((merged[head] + 1) << 16)
+    for which, sched in (("fwdp", fp), ("bwdp", bp)):
+        items = lay.xcd_items(which).reshape(-1, bd.SA_SCHED_FIELDS)
+        got = sorted(tuple(r) for r in items.tolist() if r[0] >= 0)
+        assert got == sorted(tuple(r) for r in sched.tolist())
+    # Main entries of two-part heads carry their index, and the first chunk of
+    # each tile the start-from-part flag.
+    for sched in (lay.fwd_schedule(), lay.bwd_schedule()):
+        for head, tile, e0, e1, slot, pf, slot0, nch in sched.tolist():
+            assert pf & 0xffff == hp[head]
+            if merged[head] < 0:
+                assert pf == hp[head]
+            else:
+                assert (pf >> 16) & 0x3fff == merged[head] + 1
+                assert bool(pf & bd.PART_INIT) == (slot == slot0)
+
+
+def test_two_part_head_workspaces_and_dtype():
+    """Merged strided heads add per-token float32 state to both workspaces, and
+    are bf16 only (checked before any launch, no GPU needed)."""
+    lib = bd.load_library()
+    n = 500
+    lay = Layout(n, [HeadPattern("strided_merged", 16), HeadPattern("local", 16),
+                     HeadPattern("strided_merged", 9)], 64, 64)
+    h = lay.header
+    assert h.num_merged == 2 and h.num_qslots == 0 and h.num_slots == 0
+    rnd = lambda x: -(-x // 256) * 256
+    size = ctypes.c_size_t(0)
+    assert lib.sparse_attn_fwd_workspace(lay.blob.ctypes.data, 3, 3, 64, 0, ctypes.byref(size)) == 0
+    assert size.value == rnd(3 * 2 * n * 64 * 4) + 2 * rnd(3 * 2 * n * 4)
+    assert lib.sparse_attn_bwd_workspace(lay.blob.ctypes.data, 3, 3, 64, 0, ctypes.byref(size)) == 0
+    assert size.value == rnd(3 * 3 * n * 4) + 3 * rnd(3 * 2 * n * 64 * 4)
+    fake = 1 << 20
+    assert lib.sparse_attn_fwd(lay.blob.ctypes.data, fake, 1, 3, 64, 1, fake, fake, fake, fake, fake,
+                               fake, 1 << 30, 0.0, None) == bd.SA_EUNSUPPORTED
