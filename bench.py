@@ -93,7 +93,7 @@ def measured_traffic(label: str, w):
     if label == "fwd_merge":
         key = f"{KERNEL_NAMES[label]}IDF16bLi{w.block_q}E"
     else:
-        key = f"{KERNEL_NAMES[label]}<{w.block_q}, {w.block_k}>"
+        key = f"{KERNEL_NAMES[label]}<{w.block_q}, {w.block_k}"  # any prefix-mask variant
     hits = [v for name, v in table.items() if key in name]
     return round(sum(hits[0])) if len(hits) == 1 else None
 
