@@ -37,7 +37,7 @@ EXPORTED = (
 )
 SA_FWD_MAIN, SA_FWD_MERGE, SA_FWD_ALL = 1, 2, 3
 SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_MERGE, SA_BWD_ALL = 1, 2, 4, 7
-SA_SCHED_FIELDS = 8
+SA_SCHED_FIELDS = 9
 
 
 class CHeadPattern(ctypes.Structure):
@@ -234,8 +234,8 @@ class Layout:
 
     def fwd_schedule(self) -> np.ndarray:
         """Rows (head, q-tile, first CSR entry, end CSR entry, partial slot, pattern index,
-        first slot of the tile, chunks of the tile); slot = slot0 = -1, chunks = 1 for
-        unsplit tiles."""
+        first slot of the tile, chunks of the tile, first entry's tile as (tile << 1) | FULL
+        or -1); slot = slot0 = -1, chunks = 1 for unsplit tiles."""
         return self._arr(self.header.fwd_sched_off, SA_SCHED_FIELDS * self.header.fwd_sched_len,
                          np.int32).reshape(-1, SA_SCHED_FIELDS)
 

@@ -92,6 +92,7 @@ inline void fill_pattern_table(const void* blob_host, const void* blob_dev, Tabl
     v.lo = reinterpret_cast<const int32_t*>(db + r.lo_off);
     v.hi = reinterpret_cast<const int32_t*>(db + r.hi_off);
     v.pre = r.pre_off ? reinterpret_cast<const int32_t*>(db + r.pre_off) : nullptr;
+    v.ident = identity_maps(r.kind);
     v.row_ptr = reinterpret_cast<const int32_t*>(db + r.row_ptr_off);
     v.col = reinterpret_cast<const int32_t*>(db + r.col_off);
     v.fflag = db + r.fflag_off;

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int prow = qt * BQ + w * 32 + l32;
-  const int tok = pv.qmap[prow];
+  const int tok = (pv.ident & 1) ? identity_token(prow, p.n) : pv.qmap[prow];
   const int lo = pv.lo[prow], hi = pv.hi[prow];
   // PRE: some pattern of the layout has key prefixes; this head's pattern may
   // still have none (no array).
@@ -173,7 +173,10 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) kidx[i] = buf_i32(kmap_rs, kt * BK + 8 * (w * IPW + i) + drow);
+    for (int i = 0; i < IPW; ++i) {
+      const int pos = kt * BK + 8 * (w * IPW + i) + drow;
+      kidx[i] = (pv.ident & 2) ? identity_token(pos, p.n) : buf_i32(kmap_rs, pos);
+    }
   };
   auto dload = [&](auto par) {
     constexpr int P = decltype(par)::value;
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
   const float c2 = p.scale_log2;
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
-    iload(win.get(e0) >> 1);
+    iload(it8[8] >> 1);  // the first entry travels in the schedule entry
     dload(std::integral_constant<int, 0>{});
     if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
 
   const int kpos = kt * BK + 32 * w + l32;
-  const int ktok = pv.kmap[kpos];
+  const int ktok = (pv.ident & 2) ? identity_token(kpos, p.n) : pv.kmap[kpos];
   bf16x8 kq[4], vq[4];
   if (ktok >= 0) {
     const bf16x8* ksrc = reinterpret_cast<const bf16x8*>(p.k + (base + ktok) * kD);
@@ -385,17 +388,23 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
   TileWindow win = tile_window(pv.row, pv.bflag, c0, c1);
   const BufRsrc qmap_rs = array_rsrc(pv.qmap), lo_rs = array_rsrc(pv.lo), hi_rs = array_rsrc(pv.hi);
   const BufRsrc lse_rs = array_rsrc(p.lse + base), dsum_rs = array_rsrc(p.dsum + base);
+  // CSC entry e; the first one travels in the schedule entry.
+  auto entry = [&](int e) { return e == c0 ? it8[8] : win.get(e); };
+  const bool qid = (pv.ident & 1) != 0;
   auto iload = [&](int step) {
-    const int r0 = (win.get(c0 + step / NSTEP) >> 1) * BQ + (step % NSTEP) * QS;
+    const int r0 = (entry(c0 + step / NSTEP) >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) qidx[i] = buf_i32(qmap_rs, r0 + 8 * (w * IPW + i) + drow);
-    if (mthr) rtok = buf_i32(qmap_rs, r0 + mrow);
+    for (int i = 0; i < IPW; ++i) {
+      const int pos = r0 + 8 * (w * IPW + i) + drow;
+      qidx[i] = qid ? identity_token(pos, p.n) : buf_i32(qmap_rs, pos);
+    }
+    if (mthr) rtok = qid ? identity_token(r0 + mrow, p.n) : buf_i32(qmap_rs, r0 + mrow);
   };
   auto gload = [&](int step, auto par) {
     constexpr int P = decltype(par)::value;
     bf16* qd = P ? q1s : q0s;
     bf16* od = P ? o1s : o0s;
-    const int ent = win.get(c0 + step / NSTEP);
+    const int ent = entry(c0 + step / NSTEP);
     const int r0 = (ent >> 1) * BQ + (step % NSTEP) * QS;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {

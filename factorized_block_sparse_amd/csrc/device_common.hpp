@@ -202,12 +202,24 @@ __device__ __forceinline__ float bf16_to_float(bf16 x) { return float(x); }
 // ---------------------------------------------------------------------------
 // Layout blob (device copy): header + per-pattern records, see sparse_attn.h.
 // ---------------------------------------------------------------------------
+// Patterns whose query (bit 0) or key (bit 1) map is the identity on [0, n):
+// a position is then its own token, -1 past n, with no load.
+__host__ __device__ inline int identity_maps(int kind) {
+  switch (kind) {
+    case SA_LOCAL: case SA_SAMEBLOCK: case SA_LOCAL_GLOBAL: return 3;
+    case SA_SUMMARY: case SA_FIXED_MERGED: return 1;
+    default: return 0;
+  }
+}
+__device__ __forceinline__ int identity_token(int pos, int n) { return pos < n ? pos : -1; }
+
 struct PatView {
   const int32_t* qmap;
   const int32_t* kmap;
   const int32_t* lo;
   const int32_t* hi;
   const int32_t* pre;  // key prefix [0, pre[p]) of each row; nullptr = all empty
+  int32_t ident;       // bit 0: query map is the identity, bit 1: key map is
   const int32_t* row_ptr;
   const int32_t* col;
   const uint8_t* fflag;
@@ -226,6 +238,7 @@ __device__ __forceinline__ PatView pattern_of_index(const uint8_t* blob, int pi)
   v.lo = reinterpret_cast<const int32_t*>(blob + rec->lo_off);
   v.hi = reinterpret_cast<const int32_t*>(blob + rec->hi_off);
   v.pre = rec->pre_off ? reinterpret_cast<const int32_t*>(blob + rec->pre_off) : nullptr;
+  v.ident = identity_maps(rec->kind);
   v.row_ptr = reinterpret_cast<const int32_t*>(blob + rec->row_ptr_off);
   v.col = reinterpret_cast<const int32_t*>(blob + rec->col_off);
   v.fflag = blob + rec->fflag_off;

@@ -189,7 +189,7 @@ void fwd_bf16_kernel(FwdParams p) {
   const bf16* vg = static_cast<const bf16*>(p.v) + base * kD;
 
   const int prow = qt * BQ + w * 32 + l32;
-  const int tok = pv.qmap[prow];
+  const int tok = (pv.ident & 1) ? identity_token(prow, p.n) : pv.qmap[prow];
   const int lo = pv.lo[prow], hi = pv.hi[prow];
   // PRE: some pattern of the layout has key prefixes; this head's pattern may
   // still have none (no array).
@@ -215,7 +215,10 @@ void fwd_bf16_kernel(FwdParams p) {
   int kidx[IPW];  // key-map entries of the next tile to load (fetched a tile early)
   auto iload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) kidx[i] = buf_i32(kmap_rs, kt * BK + 8 * (w * IPW + i) + drow);
+    for (int i = 0; i < IPW; ++i) {
+      const int pos = kt * BK + 8 * (w * IPW + i) + drow;
+      kidx[i] = (pv.ident & 2) ? identity_token(pos, p.n) : buf_i32(kmap_rs, pos);
+    }
   };
   auto dload = [&](auto par) {
     constexpr int P = decltype(par)::value;
@@ -256,7 +259,7 @@ void fwd_bf16_kernel(FwdParams p) {
 
   TileWindow win = tile_window(pv.col, pv.fflag, e0, e1);
   if (e0 < e1) {
-    iload(win.get(e0) >> 1);
+    iload(it8[8] >> 1);  // the first entry travels in the schedule entry
     dload(std::integral_constant<int, 0>{});
     if (e0 + 1 < e1) iload(win.get(e0 + 1) >> 1);
   }

@@ -309,6 +309,7 @@ struct SchedItem {
   int32_t head, tile, work;
   int32_t e0 = 0, e1 = 0, slot = -1;
   int32_t pattern = 0, slot0 = -1, nchunks = 1;  // head's pattern; split tile: its slots
+  int32_t first = -1;  // first list entry packed as (tile << 1) | FULL; -1 if none
 };
 
 // Per-XCD lists over the sorted schedule `sorted` (work in sorted order):
@@ -351,14 +352,15 @@ int32_t xcd_lists(const std::vector<SchedItem>& sorted, std::vector<int32_t>& ou
 }
 
 // Heaviest first; ties keep (head, tile) order.  SA_SCHED_FIELDS ints per
-// entry: (head, tile, e0, e1, slot, pattern, slot0, nchunks).
+// entry: (head, tile, e0, e1, slot, pattern, slot0, nchunks, first).
 std::vector<int32_t> sorted_schedule(std::vector<SchedItem>& items) {
   std::stable_sort(items.begin(), items.end(),
                    [](const SchedItem& a, const SchedItem& b) { return a.work > b.work; });
   std::vector<int32_t> out;
   out.reserve(items.size() * SA_SCHED_FIELDS);
   for (const auto& it : items)
-    out.insert(out.end(), {it.head, it.tile, it.e0, it.e1, it.slot, it.pattern, it.slot0, it.nchunks});
+    out.insert(out.end(),
+               {it.head, it.tile, it.e0, it.e1, it.slot, it.pattern, it.slot0, it.nchunks, it.first});
   return out;
 }
 
@@ -514,6 +516,21 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       bwdp_items.push_back(it);
     }
   }
+  // The first entry of each item's list, so a workgroup can start its first
+  // tile's loads without reading the list.
+  auto set_first = [&](std::vector<SchedItem>& items, bool csc) {
+    for (auto& it : items) {
+      if (it.e0 >= it.e1) continue;
+      const Pattern& P = pats[it.pattern & 0xffff];
+      const int32_t tile = csc ? P.row[it.e0] : P.col[it.e0];
+      const uint8_t flag = csc ? P.bflag[it.e0] : P.fflag[it.e0];
+      it.first = (tile << 1) | (flag == SA_TILE_FULL ? 1 : 0);
+    }
+  };
+  set_first(fwd_items, false);
+  set_first(fwdp_items, false);
+  set_first(bwd_items, true);
+  set_first(bwdp_items, true);
   const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
   const std::vector<int32_t> fwdp_sched = sorted_schedule(fwdp_items);

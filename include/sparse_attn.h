@@ -145,8 +145,8 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 9u
-#define SA_SCHED_FIELDS 8
+#define SA_BLOB_VERSION 10u
+#define SA_SCHED_FIELDS 9
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
  * many rows (rounded down to whole query tiles, at least one) for the dK/dV
@@ -194,9 +194,10 @@ typedef struct {
   int64_t pattern_off;      /* sa_pattern_rec[num_patterns] */
   int64_t fwd_sched_off;    /* int32[SA_SCHED_FIELDS * fwd_sched_len]: (head, q-tile,
                                first CSR entry, end CSR entry, partial slot, pattern index
-                               of the head, first slot of the tile, chunks of the tile),
-                               heaviest first; unsplit tiles have slot = slot0 = -1 and
-                               chunks = 1 */
+                               of the head, first slot of the tile, chunks of the tile,
+                               the first CSR entry's k-tile packed as (tile << 1) | FULL or
+                               -1 for an empty list), heaviest first; unsplit tiles have
+                               slot = slot0 = -1 and chunks = 1 */
   int64_t bwd_sched_off;    /* int32[SA_SCHED_FIELDS * bwd_sched_len]: the same fields over
                                k-tiles and CSC entries */
   int32_t fwd_sched_len, bwd_sched_len;

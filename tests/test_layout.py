@@ -143,13 +143,16 @@ def test_schedules_cover_every_tile_heaviest_first():
     fs, bs = lay.fwd_schedule(), lay.bwd_schedule()
     fwork, bwork = [], []
     hp = lay.head_pattern_index()
-    for head, qt, e0, e1, slot, pat, slot0, nch in fs:
+    for head, qt, e0, e1, slot, pat, slot0, nch, first in fs:
         assert (pat, slot0, nch) == (hp[head], -1, 1)
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
         assert (e0, e1, slot) == (a["row_ptr"][qt], a["row_ptr"][qt + 1], -1)  # no split at n=1000
+        assert first == (a["col"][e0] << 1) | a["fflag"][e0]
         fwork.append(e1 - e0)
-    for head, kt, e0, e1, slot, pat, slot0, nch in bs:
+    for head, kt, e0, e1, slot, pat, slot0, nch, first in bs:
         assert pat == hp[head]
+        a = lay.pattern_arrays(int(hp[head]))
+        assert first == ((a["row"][e0] << 1) | a["bflag"][e0] if e0 < e1 else -1)
         bwork.append(e1 - e0)
     assert all(w > 0 for w in fwork)
     assert fwork == sorted(fwork, reverse=True) and bwork == sorted(bwork, reverse=True)
@@ -537,7 +540,7 @@ def test_strided_merged_parts_are_disjoint_layouts_of_the_union(n, bq, bk, l):
     assert sorted((int(r[0]), int(r[1])) for r in fp) == [(hh, q) for hh in (0, 2) for q in nq]
     assert sorted((int(r[0]), int(r[1])) for r in bp) == [(hh, k) for hh in (0, 2) for k in nk]
     for sched, ptr in ((fp, arr["row_ptr"]), (bp, arr["col_ptr"])):
-        for head, tile, e0, e1, slot, pf, slot0, nch in sched.tolist():
+        for head, tile, e0, e1, slot, pf, slot0, nch, first in sched.tolist():
             assert (e0, e1, slot, slot0, nch) == (ptr[tile], ptr[tile + 1], -1, -1, 1)
             assert pf == int(part[0]) | ((merged[head] + 1) << 16)
     for which, sched in (("fwdp", fp), ("bwdp", bp)):
@@ -547,7 +550,7 @@ def test_strided_merged_parts_are_disjoint_layouts_of_the_union(n, bq, bk, l):
     # Main entries of two-part heads carry their index, and the first chunk of
     # each tile the start-from-part flag.
     for sched in (lay.fwd_schedule(), lay.bwd_schedule()):
-        for head, tile, e0, e1, slot, pf, slot0, nch in sched.tolist():
+        for head, tile, e0, e1, slot, pf, slot0, nch, first in sched.tolist():
             assert pf & 0xffff == hp[head]
             if merged[head] < 0:
                 assert pf == hp[head]
