@@ -155,7 +155,7 @@ typedef struct {
  * way for the forward and dQ passes; chunk results are merged in a fixed
  * order.  A cap of at least n disables splitting. */
 #define SA_SPLIT_ROWS 1536
-#define SA_SPLIT_KEYS 2048
+#define SA_SPLIT_KEYS 3072
 /* Number of accelerator complex dies (XCDs, each with its own L2) that
  * workgroups are dealt to round-robin on MI355X. */
 #define SA_XCDS 8

@@ -40,7 +40,7 @@ SMALL = [
     ("split_k32", 2, 1500, 64, 32, [HeadPattern("local", 1400), HeadPattern("stride", 1)], 1024),
     ("split_q128_k64", 1, 2200, 128, 64, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
                                           HeadPattern("sameblock", 2048)], 1024),
-    ("split_default_caps", 1, 2600, 64, 64, [HeadPattern("local", 2500), HeadPattern("summary", 64, 16, 2)]),
+    ("split_default_caps", 1, 3500, 64, 64, [HeadPattern("local", 3300), HeadPattern("summary", 64, 16, 2)]),
     # heads whose rows read a key prefix besides an interval (merged fixed; local + global tokens)
     ("merged_global_tiles64", 2, 700, 64, 64, [HeadPattern("fixed_merged", 128, 32, 0),
                                                HeadPattern("fixed_merged", 128, 32, 3),

@@ -241,11 +241,11 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
 ])
 def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
     """Each query tile's CSR list is covered exactly once by forward / dQ items, in
-    contiguous chunks of at most split_keys (default 2048) keys; split tiles own
+    contiguous chunks of at most split_keys (default 3072) keys; split tiles own
     consecutive slots that the merge schedule lists."""
     lay = Layout(n, heads, bq, bk)
     h = lay.header
-    assert h.split_keys == 2048
+    assert h.split_keys == 3072
     qcap = max(1, h.split_keys // bk)
     fs, cs = lay.fwd_schedule(), lay.combine_schedule()
     slots = sorted(int(r[4]) for r in fs if r[4] >= 0)
@@ -272,8 +272,9 @@ def test_query_chunks_partition_every_csr_row(n, bq, bk, heads):
                 grp = {(int(r[5]), int(r[6]), int(r[7])) for r in fs if r[0] == head and r[1] == qt}
                 assert grp == {(int(lay.head_pattern_index()[head]), s0, nch)}
     if n == 12288:
-        # summary heads read up to 3072 keys per row; strided heads stay within one class
-        assert (h.comb_sched_len > 0) == any(p.kind == "summary" for p in heads)
+        # summary heads read up to 3072 keys per row (the default cap), strided heads
+        # stay within one class: nothing is split
+        assert h.comb_sched_len == 0
 
 
 @pytest.mark.parametrize("split_keys,split_rows", [(256, 320), (96, 64), (1 << 30, 1 << 30)])
@@ -448,7 +449,8 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert lib.sparse_attn_fwd_workspace(hb, 2, 2, 64, 0, ctypes.byref(size)) == 0
     assert size.value == 0  # no query tile is split at n=128
     assert lib.sparse_attn_fwd_workspace(hb, 2, 2, 128, 0, ctypes.byref(size)) == bd.SA_EUNSUPPORTED
-    big = Layout(12288, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0)], 64, 64)
+    big = Layout(12288, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0)], 64, 64,
+                 split_keys=2048)
     assert big.header.num_qslots > 0
     assert lib.sparse_attn_fwd_workspace(big.blob.ctypes.data, 3, 2, 64, 0, ctypes.byref(size)) == 0
     rows = 3 * big.header.num_qslots * 64
