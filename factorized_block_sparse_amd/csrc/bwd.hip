@@ -468,12 +468,29 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
       floatx16 dp = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
                      n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
       const int qr = 32 * qb + sigma32(l32);
+      // All operands of the S and dP products first, then the products.
+      bf16x8 qop[4], oop[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int off = swz(qr, g + 2 * c);
-        s = mfma_bf16(*reinterpret_cast<const bf16x8*>(&qcur[off]), kq[c], s);
-        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&ocur[off]), vq[c], dp);
+        qop[c] = *reinterpret_cast<const bf16x8*>(&qcur[off]);
+        oop[c] = *reinterpret_cast<const bf16x8*>(&ocur[off]);
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s = mfma_bf16(qop[c], kq[c], s);
+        dp = mfma_bf16(oop[c], vq[c], dp);
+      }
+      // Transposed operands of the dV and dK products, read before the
+      // softmax so that their latency overlaps it.
+      bf16x8 ot[2][2], qtr[2][2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+          ot[h8][fb] = load_a_transposed_swz(ocur, 32 * qb + 16 * h8, 32 * fb, lane);
+          qtr[h8][fb] = load_a_transposed_swz(qcur, 32 * qb + 16 * h8, 32 * fb, lane);
+        }
       if (!full) {
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
@@ -518,9 +535,8 @@ __global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 sb = pack_bf16x8(&ds[8 * h8]);
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
-          const int q0 = 32 * qb + 16 * h8;
-          dva[fb] = mfma_bf16(load_a_transposed_swz(ocur, q0, 32 * fb, lane), pb, dva[fb]);
-          dka[fb] = mfma_bf16(load_a_transposed_swz(qcur, q0, 32 * fb, lane), sb, dka[fb]);
+          dva[fb] = mfma_bf16(ot[h8][fb], pb, dva[fb]);
+          dka[fb] = mfma_bf16(qtr[h8][fb], sb, dka[fb]);
         }
       }
     }
