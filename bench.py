@@ -85,6 +85,11 @@ KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "fwd_merge": "fwd_merge_kernel", "bwd_
                 "bwd_dkdv": "bwd_dkdv_kernel", "bwd_merge": "bwd_merge_kernel"}
 
 
+def kernel_sources_hash() -> str:
+    from factorized_block_sparse_amd import profiling
+    return profiling.source_hash()
+
+
 def measured_traffic(label: str, w):
     """HBM bytes (fetched + written) per launch of this kernel, from the committed
     counter summary; None when there is none or the kernel sources changed since."""
@@ -650,6 +655,7 @@ def main():
                    "per_workload": per_wl, "kernels": kernels},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "kernel_sources_sha256": kernel_sources_hash(),
     }
     print(json.dumps(line))
 

@@ -18,12 +18,18 @@
 //             operands and dK, dV accumulated in registers; per query tile,
 //             Q, dO (row-major), LSE and D are staged in LDS; S = Q K^T and
 //             dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T
-//             through transposing LDS reads).  Unsplit tiles write dK, dV
-//             (exact zeros for keys no query reads).
+//             through transposing LDS reads, issued before the softmax so
+//             their latency overlaps it).  Unsplit tiles write dK, dV (exact
+//             zeros for keys no query reads).
 // Chunks of split tiles store float32 partial sums in the workspace; a third
 // launch (bwd_merge) sums the chunks of every split key tile (dK, dV) and
 // split query tile (dQ) in chunk order and writes their gradients.  No
 // atomics: every result is deterministic.
+//
+// Merged strided heads run in two parts with disjoint key sets: before each
+// of the two passes, a launch of the same kernel over the second parts stores
+// each token's dQ (or dK, dV) sums in the workspace, and the first chunk of
+// each main tile of such a head starts from them.
 
 #include <limits.h>
 #include <math.h>

@@ -27,8 +27,14 @@
 //
 // Query tiles with long CSR lists run as several chunks (one workgroup each).
 // A chunk stores its unnormalised O, running max and running sum in float32;
-// a second launch merges the chunks of each split tile exactly (rescaling
+// a further launch merges the chunks of each split tile exactly (rescaling
 // each to the common max) in chunk order.
+//
+// Merged strided heads run in two parts with disjoint key sets (see the
+// layout builder): a launch of the same kernel over the second parts stores
+// each token's softmax state (unnormalised O, running max, running sum) in
+// the workspace, and the first chunk of each main tile of such a head starts
+// its online softmax from that state.
 
 #include <math.h>
 

@@ -15,11 +15,13 @@ Two kinds of summary, both short text files:
   bank conflicts, wait cycles), averaged per dispatch, with the ratios
   derived from them.
 
-Usage (on the csv files a profiling run wrote):
+Usage (on the csv files a profiling run wrote; ``--log <stdout of the
+profiled run>`` records the kernel-source hash that run's bench line printed,
+otherwise the hash of the sources here):
 
     python -m factorized_block_sparse_amd.profiling stats <kernel_stats.csv> <out.txt> "<command>"
     python -m factorized_block_sparse_amd.profiling traffic <fetch.csv> <write.csv> <copy MiB> \\
-        <out.txt> "<fetch command>" "<write command>"
+        <out.txt> "<fetch command>" "<write command>" [<kernel_stats.csv>]
     python -m factorized_block_sparse_amd.profiling counters <counters.csv> <out.txt> "<command>"
 """
 
@@ -51,11 +53,23 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def write_kernel_stats(src: str, dst: str, command: str) -> str:
+def run_hash(log: str | None) -> str:
+    """The kernel-source hash of the profiled run: read from the bench line in
+    its log (bench.py prints it); without a log, the hash of the sources here."""
+    if log:
+        import json
+        for line in open(log, errors="replace"):
+            if line.startswith("{") and "kernel_sources_sha256" in line:
+                return json.loads(line)["kernel_sources_sha256"]
+        raise SystemExit(f"no bench line with kernel_sources_sha256 in {log}")
+    return source_hash()
+
+
+def write_kernel_stats(src: str, dst: str, command: str, log: str | None = None) -> str:
     rows = list(csv.DictReader(open(src)))
     lines = ["# rocprofv3 kernel statistics (one MI355X)",
              f"# command: {command}",
-             f"# kernel sources sha256: {source_hash()}",
+             f"# kernel sources sha256: {run_hash(log)}",
              f"{'kernel':58s} {'calls':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
     for r in rows:
         lines.append(f"{r['Name'][:58]:58s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:9.2f} "
@@ -85,9 +99,18 @@ def _first_copy(path: str) -> float:
     return min(hits)[1]
 
 
+def _avg_durations_us(stats_csv: str | None) -> dict:
+    if not stats_csv:
+        return {}
+    return {r["Name"]: float(r["AverageNs"]) / 1e3 for r in csv.DictReader(open(stats_csv))}
+
+
 def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, dst: str, fetch_cmd: str,
-                  write_cmd: str) -> str:
+                  write_cmd: str, stats_csv: str | None = None, log: str | None = None) -> str:
+    """Per-dispatch HBM bytes; with the kernel statistics of a kernel-trace run
+    of the same command, also the achieved HBM rate (bytes / average duration)."""
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
+    dur = _avg_durations_us(stats_csv)
     copy_f, copy_w = _first_copy(fetch_csv), _first_copy(write_csv)
     known_kib = copy_mib * 1024.0
     f_scale = known_kib / copy_f
@@ -98,14 +121,16 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, dst: str, fetch
              f"# calibration: the first dispatch of the copy kernel (a {copy_mib} MiB device-to-device "
              f"copy) counts {copy_f:.1f} KiB fetched and {copy_w:.1f} KiB written;",
              f"#   scale factors fetch x{f_scale:.4f}, write x{w_scale:.4f} (known / counted)",
-             f"# kernel sources sha256: {source_hash()}",
-             "# kernel | dispatches | fetch_MB | write_MB  (scaled, per dispatch, 1 MB = 1e6 B)"]
+             f"# kernel sources sha256: {run_hash(log)}",
+             "# kernel | dispatches | fetch_MB | write_MB | achieved_GB/s  (scaled, per dispatch, "
+             "1 MB = 1e6 B; GB/s = (fetch + write) / kernel-trace average duration, - if none)"]
     for k in sorted(fetch, key=lambda x: -fetch[x][0]):
         if COPY_KERNEL_MARK in k or k not in write or "sa::" not in k and "_ZN2sa" not in k:
             continue
         fb = fetch[k][0] * f_scale * 1024
         wb = write[k][0] * w_scale * 1024
-        lines.append(f"{k} | {fetch[k][1]} | {fb / 1e6:.3f} | {wb / 1e6:.3f}")
+        rate = f"{(fb + wb) / (dur[k] * 1e-6) / 1e9:.0f}" if k in dur else "-"
+        lines.append(f"{k} | {fetch[k][1]} | {fb / 1e6:.3f} | {wb / 1e6:.3f} | {rate}")
     text = "\n".join(lines) + "\n"
     with open(dst, "w") as f:
         f.write(text)
@@ -122,7 +147,7 @@ def _per_kernel_counters(path: str) -> dict:
     return {k: {c: (sum(v) / len(v), len(v)) for c, v in d.items()} for k, d in vals.items()}
 
 
-def write_counters(src: str, dst: str, command: str) -> str:
+def write_counters(src: str, dst: str, command: str, log: str | None = None) -> str:
     """Per-dispatch averages of SQ counters and three ratios:
     mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (128 x GRBM_GUI_ACTIVE), the share
     of SIMD cycles the matrix units were busy.  GRBM_GUI_ACTIVE reads about 8x
@@ -138,7 +163,7 @@ def write_counters(src: str, dst: str, command: str) -> str:
     names = sorted({c for d in table.values() for c in d})
     lines = ["# rocprofv3 shader counters per dispatch (one MI355X)",
              f"# command: {command}",
-             f"# kernel sources sha256: {source_hash()}",
+             f"# kernel sources sha256: {run_hash(log)}",
              "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (128 SIMDs per XCD x GRBM_GUI_ACTIVE, "
              "which counts once per XCD); lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS; "
              "wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES",
@@ -170,18 +195,24 @@ def read_traffic(path: str) -> tuple[str | None, dict]:
         if line.startswith("# kernel sources sha256:"):
             recorded = line.split(":", 1)[1].strip()
         elif not line.startswith("#") and "|" in line:
-            name, _, fmb, wmb = (x.strip() for x in line.split("|"))
+            name, _, fmb, wmb = (x.strip() for x in line.split("|")[:4])
             table[name] = (float(fmb) * 1e6, float(wmb) * 1e6)
     return recorded, table
 
 
 def main(argv: list[str]) -> None:
+    log = None
+    if "--log" in argv:  # the profiled run's stdout: the hash is taken from its bench line
+        i = argv.index("--log")
+        log = argv[i + 1]
+        argv = argv[:i] + argv[i + 2:]
     if len(argv) >= 4 and argv[0] == "stats":
-        print(write_kernel_stats(argv[1], argv[2], argv[3]))
+        print(write_kernel_stats(argv[1], argv[2], argv[3], log))
     elif len(argv) >= 4 and argv[0] == "counters":
-        print(write_counters(argv[1], argv[2], argv[3]))
+        print(write_counters(argv[1], argv[2], argv[3], log))
     elif len(argv) >= 7 and argv[0] == "traffic":
-        print(write_traffic(argv[1], argv[2], int(argv[3]), argv[4], argv[5], argv[6]))
+        print(write_traffic(argv[1], argv[2], int(argv[3]), argv[4], argv[5], argv[6],
+                            argv[7] if len(argv) > 7 else None, log))
     else:
         print(__doc__)
         sys.exit(2)
