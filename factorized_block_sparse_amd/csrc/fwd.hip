@@ -165,11 +165,12 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams& p, const floatx16 
 // --------------------------------------------------------------------------
 // bfloat16 inputs, 32x32x16 bf16 MFMA
 // --------------------------------------------------------------------------
-// Occupancy target 3 waves per SIMD: the register allocation then leaves the
-// scheduler room to overlap the next tile's LDS reads and MFMAs with the
-// softmax (measured faster than the 4 waves the kernel could fit).
+// Occupancy: 2 waves per SIMD for query tiles of 64 and more rows (measured
+// faster than 3: with two 128-row workgroups per CU, fewer long query tiles
+// run at once and the longest-first list order evens out the CUs' work), and
+// up to 3 for 32-row tiles (one-wave workgroups, 10 per CU by LDS).
 template <int BQ, int BK, bool PRE>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(BQ >= 64 ? 3 : 2, BQ >= 64 ? 3 : 2)))
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, BQ >= 64 ? 2 : 3)))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int NW = BQ / 32;
   constexpr int NKB = BK / 32;
