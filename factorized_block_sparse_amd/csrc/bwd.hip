@@ -715,7 +715,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
   if (rc != SA_OK) return rc;
   if (dtype != SA_BF16) return SA_EUNSUPPORTED;
   const int bq = li.block_q, bk = li.block_k;
-  if (!(bq == 32 || bq == 64 || bq == 128) || !(bk == 32 || bk == 64)) return SA_EUNSUPPORTED;
+  if (!(bq == 32 || bq == 64 || bq == 128) || !(bk == 32 || bk == 64 || (bq == 128 && bk == 128)))
+    return SA_EUNSUPPORTED;
   float sc;
   rc = resolve_scale(scale, d, &sc);
   if (rc != SA_OK) return rc;
@@ -800,7 +801,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 64 && bk == 32) SA_LAUNCH_PART((bwd_dq_kernel<64, 32, false>), gqp, 128);
     else if (bq == 64 && bk == 64) SA_LAUNCH_PART((bwd_dq_kernel<64, 64, false>), gqp, 128);
     else if (bq == 128 && bk == 32) SA_LAUNCH_PART((bwd_dq_kernel<128, 32, false>), gqp, 256);
-    else SA_LAUNCH_PART((bwd_dq_kernel<128, 64, false>), gqp, 256);
+    else if (bq == 128 && bk == 64) SA_LAUNCH_PART((bwd_dq_kernel<128, 64, false>), gqp, 256);
+    else SA_LAUNCH_PART((bwd_dq_kernel<128, 128, false>), gqp, 256);
   }
   if ((phases & SA_BWD_DQ) && gq > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 32, 32, gq, 64);
@@ -808,7 +810,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 64 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 64, 32, gq, 128);
     else if (bq == 64 && bk == 64) SA_LAUNCH_P(bwd_dq_kernel, 64, 64, gq, 128);
     else if (bq == 128 && bk == 32) SA_LAUNCH_P(bwd_dq_kernel, 128, 32, gq, 256);
-    else SA_LAUNCH_P(bwd_dq_kernel, 128, 64, gq, 256);
+    else if (bq == 128 && bk == 64) SA_LAUNCH_P(bwd_dq_kernel, 128, 64, gq, 256);
+    else SA_LAUNCH_P(bwd_dq_kernel, 128, 128, gq, 256);
   }
   if ((phases & SA_BWD_DKDV) && gkp > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH_PART((bwd_dkdv_kernel<32, 32, false>), gkp, 64);
@@ -816,7 +819,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 128 && bk == 32) SA_LAUNCH_PART((bwd_dkdv_kernel<128, 32, false>), gkp, 64);
     else if (bq == 32 && bk == 64) SA_LAUNCH_PART((bwd_dkdv_kernel<32, 64, false>), gkp, 128);
     else if (bq == 64 && bk == 64) SA_LAUNCH_PART((bwd_dkdv_kernel<64, 64, false>), gkp, 128);
-    else SA_LAUNCH_PART((bwd_dkdv_kernel<128, 64, false>), gkp, 128);
+    else if (bq == 128 && bk == 64) SA_LAUNCH_PART((bwd_dkdv_kernel<128, 64, false>), gkp, 128);
+    else SA_LAUNCH_PART((bwd_dkdv_kernel<128, 128, false>), gkp, 256);
   }
 #undef SA_LAUNCH_PART
   if ((phases & SA_BWD_DKDV) && gk > 0) {
@@ -825,7 +829,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 128 && bk == 32) SA_LAUNCH_P(bwd_dkdv_kernel, 128, 32, gk, 64);
     else if (bq == 32 && bk == 64) SA_LAUNCH_P(bwd_dkdv_kernel, 32, 64, gk, 128);
     else if (bq == 64 && bk == 64) SA_LAUNCH_P(bwd_dkdv_kernel, 64, 64, gk, 128);
-    else SA_LAUNCH_P(bwd_dkdv_kernel, 128, 64, gk, 128);
+    else if (bq == 128 && bk == 64) SA_LAUNCH_P(bwd_dkdv_kernel, 128, 64, gk, 128);
+    else SA_LAUNCH_P(bwd_dkdv_kernel, 128, 128, gk, 256);
   }
   if ((phases & SA_BWD_MERGE) && gm > 0) {
     if (bq == 32 && bk == 32) SA_LAUNCH((bwd_merge_kernel<32, 32>), gm, 256);
@@ -833,7 +838,8 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 64 && bk == 32) SA_LAUNCH((bwd_merge_kernel<64, 32>), gm, 256);
     else if (bq == 64 && bk == 64) SA_LAUNCH((bwd_merge_kernel<64, 64>), gm, 256);
     else if (bq == 128 && bk == 32) SA_LAUNCH((bwd_merge_kernel<128, 32>), gm, 256);
-    else SA_LAUNCH((bwd_merge_kernel<128, 64>), gm, 256);
+    else if (bq == 128 && bk == 64) SA_LAUNCH((bwd_merge_kernel<128, 64>), gm, 256);
+    else SA_LAUNCH((bwd_merge_kernel<128, 128>), gm, 256);
   }
 #undef SA_LAUNCH_P
 #undef SA_LAUNCH

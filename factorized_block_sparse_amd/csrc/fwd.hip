@@ -605,7 +605,8 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
   sa_blob_header h;
   memcpy(&h, blob_host, sizeof(h));
   const int bq = li.block_q, bk = li.block_k;
-  const bool shape_ok = dtype == SA_BF16 ? (bk == 32 || bk == 64) : (bk == 32);
+  const bool shape_ok =
+      dtype == SA_BF16 ? (bk == 32 || bk == 64 || (bq == 128 && bk == 128)) : (bk == 32);
   if (!shape_ok) return SA_EUNSUPPORTED;
   if (dtype != SA_BF16 && li.num_merged > 0) return SA_EUNSUPPORTED;  // two-part heads: bf16 only
   if (B == 0 || li.fwd_xl_len == 0) return SA_OK;  // empty batch: pointers may be NULL
@@ -671,7 +672,8 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
     else if (bq == 64 && bk == 32) SA_LAUNCH_PART(64, 32, 128);
     else if (bq == 64 && bk == 64) SA_LAUNCH_PART(64, 64, 128);
     else if (bq == 128 && bk == 32) SA_LAUNCH_PART(128, 32, 256);
-    else SA_LAUNCH_PART(128, 64, 256);
+    else if (bq == 128 && bk == 64) SA_LAUNCH_PART(128, 64, 256);
+    else SA_LAUNCH_PART(128, 128, 256);
 #undef SA_LAUNCH_PART
   }
   if (phases & SA_FWD_MAIN) {
@@ -681,7 +683,8 @@ extern "C" int sparse_attn_fwd_phases(const void* blob_host, const void* blob_de
       else if (bq == 64 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 64, 32, grid, 128);
       else if (bq == 64 && bk == 64) SA_LAUNCH_P(fwd_bf16_kernel, 64, 64, grid, 128);
       else if (bq == 128 && bk == 32) SA_LAUNCH_P(fwd_bf16_kernel, 128, 32, grid, 256);
-      else SA_LAUNCH_P(fwd_bf16_kernel, 128, 64, grid, 256);
+      else if (bq == 128 && bk == 64) SA_LAUNCH_P(fwd_bf16_kernel, 128, 64, grid, 256);
+      else SA_LAUNCH_P(fwd_bf16_kernel, 128, 128, grid, 256);
     } else {
       if (bq == 32) SA_LAUNCH_P(fwd_f32_kernel, 32, 32, grid, 64);
       else if (bq == 64) SA_LAUNCH_P(fwd_f32_kernel, 64, 32, grid, 128);

@@ -71,6 +71,16 @@ SMALL = [
     ("strided_merged_q128_k64", 1, 640, 128, 64, [HeadPattern("strided_merged", 40)]),
     ("split_strided_merged", 1, 2300, 64, 64, [HeadPattern("strided_merged", 1100),
                                                HeadPattern("strided_merged", 16)], 512),
+    # 128-key tiles (four waves of 32 keys in the dK/dV pass)
+    ("fixed_tiles128", 1, 768, 128, 128, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
+                                          HeadPattern("summary", 128, 32, 3), HeadPattern("local", 100)]),
+    ("ragged_tiles128", 1, 333, 128, 128, [HeadPattern("local", 17), HeadPattern("stride", 17),
+                                           HeadPattern("sameblock", 20), HeadPattern("summary", 20, 3, 1),
+                                           HeadPattern("fixed_merged", 20, 3, 1),
+                                           HeadPattern("local_global", 17, 5),
+                                           HeadPattern("strided_merged", 7)]),
+    ("split_tiles128", 1, 2200, 128, 128, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
+                                           HeadPattern("sameblock", 2048)], 1024),
 ]
 
 

@@ -579,3 +579,21 @@ def test_two_part_head_workspaces_and_dtype():
     fake = 1 << 20
     assert lib.sparse_attn_fwd(lay.blob.ctypes.data, fake, 1, 3, 64, 1, fake, fake, fake, fake, fake,
                                fake, 1 << 30, 0.0, None) == bd.SA_EUNSUPPORTED
+
+
+def test_key_tiles_of_128_need_query_tiles_of_128():
+    """128-key tiles run only with 128-row query tiles (bf16); other shapes with
+    128-key tiles are rejected before any launch (no GPU needed)."""
+    lib = bd.load_library()
+    fake = 1 << 20
+    heads = [HeadPattern("local", 16), HeadPattern("stride", 16)]
+    for bq, bk, want in ((64, 128, bd.SA_EUNSUPPORTED), (32, 128, bd.SA_EUNSUPPORTED)):
+        lay = Layout(300, heads, bq, bk)
+        hb = lay.blob.ctypes.data
+        assert lib.sparse_attn_fwd(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake,
+                                   fake, 1 << 30, 0.0, None) == want
+        assert lib.sparse_attn_bwd(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, fake, fake, 1 << 30, 0.0, None) == want
+    lay = Layout(300, heads, 128, 128)
+    assert lib.sparse_attn_fwd(lay.blob.ctypes.data, fake, 1, 2, 64, 1, fake, fake, fake, fake, fake,
+                               fake, 1 << 30, 0.0, None) == bd.SA_EUNSUPPORTED  # float32: 32-key tiles only
