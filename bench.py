@@ -373,7 +373,7 @@ def crossover(args) -> None:
     for n in (512, 1024, 2048, 4096, 8192, 16384):
         B = max(1, 16384 // n)
         l = 1 << round(math.log2(math.sqrt(n)))
-        dense = time_config(torch, bd, W, n, tuple(W.HeadSpec(W.LOCAL, n) for _ in range(8)), 128, 64,
+        dense = time_config(torch, bd, W, n, tuple(W.HeadSpec(W.LOCAL, n) for _ in range(8)), 128, 128,
                             B, 3000 + n, args.steps, args.warmup)
         sparse = min((time_config(torch, bd, W, n, W.strided_heads(8, l), t, t, B, 3000 + n,
                                   args.steps, args.warmup) for t in (32, 64)),
@@ -432,7 +432,7 @@ def summary_width(args) -> None:
     n, l = 12288, 128
     for c in (8, 16, 32):
         heads = W.fixed_heads(8, l, c)
-        for bq, bk in ((128, 64), (64, 64)):
+        for bq, bk in ((128, 128), (128, 64)):
             r = time_config(torch, bd, W, n, heads, bq, bk, 2, 4000 + c, args.steps, args.warmup)
             natural = 2 * sum(natural_order_tile_area(n, h, bq, bk) for h in heads)
             r.update(mode="summary_width", l=l, c=c,

@@ -314,12 +314,16 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
 // --------------------------------------------------------------------------
 // dK/dV pass: one workgroup per (key tile, chunk of its CSC list).
 // BK = 32 * NW keys; query tiles of BQ rows are processed in steps of
-// QS = min(BQ, 64) rows.
+// QS = min(BQ, 64) rows, or of all 128 rows with 128-key tiles (four waves
+// share each staged Q / dO tile: half the barriers and staging per key).
 // --------------------------------------------------------------------------
+// Workgroups of two or more waves: held to two waves per SIMD (256 registers;
+// the prefix compares would otherwise take one more and halve the occupancy).
 template <int BQ, int BK, bool PRE>
-__global__ __launch_bounds__(BK * 2) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BK * 2) __attribute__((amdgpu_waves_per_eu(BK >= 64 ? 2 : 1, 2)))
+void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = BK / 32;
-  constexpr int QS = BQ < 64 ? BQ : 64;
+  constexpr int QS = BK == 128 ? 128 : (BQ < 64 ? BQ : 64);
   constexpr int NSTEP = BQ / QS;
   constexpr int NQB = QS / 32;
   constexpr int IPW = QS / 8 / NW;  // 1 KB direct loads per wave, tensor and step

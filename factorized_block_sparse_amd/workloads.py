@@ -86,7 +86,7 @@ WORKLOADS = {
                  note="strided pattern, forward only, float32, 32x32 tiles"),
         Workload("strided_n3072", 4, 8, 3072, 64, strided_heads(8, 64), "bf16", 64, 64, 1002,
                  note="strided pattern at the CIFAR-10 context length"),
-        Workload("fixed_n12288", 2, 8, 12288, 64, fixed_heads(8, 128, 32), "bf16", 128, 64, 1003,
+        Workload("fixed_n12288", 2, 8, 12288, 64, fixed_heads(8, 128, 32), "bf16", 128, 128, 1003,
                  note="fixed pattern at the Enwik8 context length, l=128, c=32"),
         Workload("strided_n12288", 1, 16, 12288, 64, strided_heads(16, 128), "bf16", 32, 32, 1004,
                  sinusoid=True,

@@ -18,6 +18,7 @@ import pytest
 
 from oracle import masks as M
 from factorized_block_sparse_amd import binding as bd
+from factorized_block_sparse_amd import workloads as W
 from factorized_block_sparse_amd.binding import HeadPattern, Layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -492,7 +493,8 @@ def test_profile_summaries_parse_and_track_the_sources(tmp_path):
     path = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
     recorded, table = profiling.read_traffic(path)
     assert recorded is not None and len(recorded) == 64
-    assert any("bwd_dkdv_kernel<128, 64" in k for k in table)
+    w = W.WORKLOADS["fixed_n12288"]
+    assert any(f"bwd_dkdv_kernel<{w.block_q}, {w.block_k}" in k for k in table)
     assert all(f > 0 and w > 0 for f, w in table.values())
     stale = tmp_path / "t.txt"
     stale.write_text(open(path).read().replace(recorded, "0" * 64))
