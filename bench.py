@@ -468,7 +468,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(the attention path is single-GPU; see the design notes for how it would shard)",
+              "(the attention path runs on one GPU; batch elements and heads would shard across "
+              "GPUs with no communication)",
               file=sys.stderr)
         sys.exit(2)
 

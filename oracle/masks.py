@@ -13,8 +13,7 @@ of {j : j <= i}).  The four head kinds are the two factorizations of section
 * fixed, head 2 (``summary``):    A_i = {j <= i : s <= j mod l <= s + c - 1}
   with s = l - c for the first summary head.
 
-Readings where the page is garbled or silent (each is listed, with its
-reason, in the design notes of the repository):
+Readings where the page is garbled or silent, each with its reason:
 
 * The summary range is printed as {t, ..., l} with t = l - c; since
   j mod l never equals l, the range taken is the c residues l - c ... l - 1.
