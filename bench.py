@@ -72,12 +72,12 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
 
 def algorithmic_bytes(w) -> int:
     """HBM bytes one forward (+ backward) of a workload must move: the forward
-    reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO and
-    LSE and writes dQ, dK, dV."""
+    reads Q, K, V and writes O and LSE; the backward reads Q, K, V, O, dO, LSE
+    and D (the per-row dO . O, one float) and writes dQ, dK, dV."""
     elt = 2 if w.dtype == "bf16" else 4
     rows = w.B * w.H * w.n
     fwd = rows * (4 * D * elt + 4)
-    return fwd + (rows * (8 * D * elt + 4) if w.backward else 0)
+    return fwd + (rows * (8 * D * elt + 8) if w.backward else 0)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
