@@ -19,7 +19,8 @@ an event, reported as event_overhead_us); then K steps with one event between
 consecutive steps (p10 / p50 / p90 of single steps); then K cache-cold steps
 that rotate three input sets; then K steps with each workload on a stream of
 its own (value_two_streams; the headline stays the one-stream value); then a
-vendor bf16 GEMM as a measured peak reference.  The layout build is timed once
+vendor bf16 GEMM as a measured peak reference and device-to-device copies as
+measured HBM and Infinity-Cache bandwidths.  The layout build is timed once
 on the host.
 
 Prints one JSON line.  ``--gpus`` above 1 exits: the path runs on one GPU.
@@ -190,6 +191,37 @@ def vendor_gemm_reference(torch):
         del a, b, c
         return {"tflops": round(2 * n ** 3 / (best * 1e-3) / 1e12, 1),
                 "what": "torch.matmul bf16 8192x8192x8192, best of 3 x 10 calls"}
+    except Exception:  # reference only; never fails the bench
+        return None
+
+
+def vendor_copy_reference(torch):
+    """Measured memory references on this GPU: device-to-device copies (the
+    vendor copy kernel) of 2 GiB, far more than the 256 MB Infinity Cache (HBM
+    bandwidth), and of 64 MiB, which stays in it (Infinity-Cache bandwidth);
+    bytes read + written per second, best of 3 timings."""
+    try:
+        out = {}
+        for key, size, reps in (("hbm_gbs", 2 << 30, 5), ("infinity_cache_gbs", 64 << 20, 50)):
+            a = torch.empty(size, device="cuda", dtype=torch.uint8)
+            b = torch.empty_like(a)
+            for _ in range(3):
+                b.copy_(a)
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    b.copy_(a)
+                e1.record()
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) / reps
+                best = t if best is None else min(best, t)
+            out[key] = round(2 * size / (best * 1e-3) / 1e9, 1)
+            del a, b
+        out["what"] = "device-to-device copies of 2 GiB and 64 MiB, (read + written bytes) / time, best of 3"
+        return out
     except Exception:  # reference only; never fails the bench
         return None
 
@@ -572,7 +604,7 @@ def main():
 
     # Step-time distribution: one event between consecutive steps (each
     # interval includes one event's cost).
-    pct, two_ms, cold_ms, gemm = (lambda f: None), None, None, None
+    pct, two_ms, cold_ms, gemm, copy = (lambda f: None), None, None, None, None
     if not args.no_extra_passes:
         sev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         sev[0].record()
@@ -592,6 +624,7 @@ def main():
         # Infinity Cache in total) so that a step does not find its inputs cached.
         cold_ms = cache_cold_step_ms(torch, bd, runs, K)
         gemm = vendor_gemm_reference(torch)
+        copy = vendor_copy_reference(torch)
 
     useful = sum(r["useful"] for r in runs)
     value = useful / (ms_per_step * 1e-3) / 1e12
@@ -615,6 +648,8 @@ def main():
                           "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                           "alg_hbm_bytes": alg_bytes,
                           "pct_hbm_roofline": round(100 * alg_bytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 2),
+                          "pct_measured_copy_bandwidth": (round(100 * alg_bytes / (ms * 1e-3) / (copy["hbm_gbs"] * 1e9), 2)
+                                                          if copy else None),
                           "pairs": r["pairs"], "tile_padding_overhead": round(r["padding"], 3),
                           "layout_build_ms": layout_ms[w.name]}
     dom = max(kernels, key=lambda k: k["ms"])
@@ -645,6 +680,7 @@ def main():
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
         "pct_of_measured_gemm": round(100 * value / gemm["tflops"], 3) if gemm else None,
         "measured_gemm_reference": gemm,
+        "measured_copy_reference": copy,
         "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "ms_per_step_cache_cold": round(cold_ms, 4) if cold_ms else None,
         "ms_per_step_two_streams": round(two_ms, 4) if two_ms else None,
