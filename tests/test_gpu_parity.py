@@ -81,6 +81,9 @@ SMALL = [
                                            HeadPattern("strided_merged", 7)]),
     ("split_tiles128", 1, 2200, 128, 128, [HeadPattern("summary", 64, 32, 0), HeadPattern("local", 2100),
                                            HeadPattern("sameblock", 2048)], 1024),
+    ("split_merged_tiles128", 1, 2300, 128, 128, [HeadPattern("fixed_merged", 128, 32, 2),
+                                                  HeadPattern("local_global", 256, 300),
+                                                  HeadPattern("strided_merged", 1100)], 512),
 ]
 
 
