@@ -328,6 +328,26 @@ def _check_qkv(layout: Layout, tensors, names):
     return B, H, n, d, dt
 
 
+def _check_like(t, ref, nm):
+    """An output tensor the kernels write through a raw pointer: same shape,
+    dtype and device as ``ref``, contiguous."""
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+        raise ValueError(f"{nm} must be a contiguous tensor of q's shape, dtype and device")
+
+
+def _check_lse(lse, B, H, n, device, nm="lse"):
+    import torch
+    if (tuple(lse.shape) != (B, H, n) or lse.dtype != torch.float32 or lse.device != device
+            or not lse.is_contiguous()):
+        raise ValueError(f"{nm} must be a contiguous float32 [B, H, n] tensor on q's device")
+
+
+def _check_workspace(ws, device):
+    import torch
+    if ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+
+
 def fwd_workspace_bytes(layout: Layout, B: int, H: int, d: int = 64, dtype: int = SA_BF16) -> int:
     lib = load_library()
     size = ctypes.c_size_t(0)
@@ -349,6 +369,10 @@ def sparse_attn_fwd(layout: Layout, q, k, v, scale: float | None = None, out=Non
     B, H, n, d, dt = _check_qkv(layout, (q, k, v), ("q", "k", "v"))
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, n), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like(o, q, "out")
+    _check_lse(lse_t, B, H, n, q.device)
+    if workspace is not None:
+        _check_workspace(workspace, q.device)
     if workspace is None:
         need = fwd_workspace_bytes(layout, B, H, d, dt)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
@@ -386,13 +410,15 @@ def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = N
     import torch
     lib = load_library()
     B, H, n, d, dt = _check_qkv(layout, (q, k, v, o, do), ("q", "k", "v", "o", "do"))
-    if lse.shape != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+    _check_lse(lse, B, H, n, q.device)
     need = bwd_workspace_bytes(layout, B, H, d, dt)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    _check_workspace(ws, q.device)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_like(t, q, nm)
     blob_dev = layout.device_blob(q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     args = (layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,

@@ -155,6 +155,31 @@ def test_empty_batch_is_a_no_op():
     assert o.numel() == 0 and dq.numel() == 0
 
 
+def test_binding_rejects_mismatched_outputs_before_any_launch():
+    """Outputs, LSE and workspaces are written through raw pointers: the binding
+    refuses tensors of the wrong shape, dtype or device instead of launching."""
+    heads = [HeadPattern("local", 8), HeadPattern("stride", 8)]
+    lay = Layout(64, heads, 64, 64)
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32, device=dev)
+    bad = [dict(out=torch.zeros((1, 2, 32, 64), dtype=torch.bfloat16, device=dev)),
+           dict(out=torch.zeros((1, 2, 64, 64), dtype=torch.float32, device=dev)),
+           dict(lse=torch.zeros((1, 2, 32), dtype=torch.float32, device=dev)),
+           dict(lse=torch.zeros((1, 2, 64), dtype=torch.bfloat16, device=dev)),
+           dict(workspace=torch.zeros(64, dtype=torch.float32, device=dev))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            bd.sparse_attn_fwd(lay, q, q, q, **kw)
+    with pytest.raises(ValueError):
+        bd.sparse_attn_bwd(lay, q, q, q, q, lse, q, grads=(q, q, q[:, :, :32]))
+    with pytest.raises(ValueError):
+        bd.sparse_attn_bwd(lay, q, q, q, q, lse[:, :1], q)
+    with pytest.raises(ValueError):
+        bd.sparse_attn_bwd(lay, q, q, q, q, lse, q, workspace=torch.zeros(8, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+
+
 def test_repeat_calls_are_bitwise_deterministic():
     """No atomics; split tiles are merged in chunk order: forward and backward reproduce
     bit for bit, with the same workspaces reused across calls."""
