@@ -305,3 +305,60 @@ def test_workload_full_size_sampled(wname):
             ref = do[b, h].sum(0)
             assert np.max(np.abs(sv - ref)) <= 1e-2 * np.abs(out["dv"][b, h]).sum(0).max() + 1e-2, (b, h)
     assert np.isfinite(out["o"]).all() and np.isfinite(out["dq"]).all()
+
+
+def _compact(tokens):
+    """Sorted token universe and a map from token arrays to indices into it."""
+    u = np.unique(np.concatenate([np.asarray(t, dtype=np.int64).ravel() for t in tokens]))
+    return u, (lambda a: np.searchsorted(u, np.asarray(a, dtype=np.int64)))
+
+
+@pytest.mark.skipif(not torch.cuda.is_available() or
+                    torch.cuda.get_device_properties(0).total_memory < (120 << 30),
+                    reason="needs a GPU with 120 GB for 8 tensors of 8.6 GB")
+def test_longest_bf16_sequence_sampled():
+    """n = 2^25 - 64, the longest bf16 sequence the kernels address (a (b, h)
+    slice spans just under 4 GB of 32-bit byte offsets): sampled rows and keys
+    at both ends against the oracle, on gathered rows, plus the gradient
+    invariants over every row on the GPU."""
+    n = (1 << 25) - 64
+    heads = [HeadPattern("local", 16), HeadPattern("stride", 1 << 20)]
+    lay = Layout(n, heads, 64, 64)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(25)
+    shape = (1, 2, n, 64)
+    q, k, v, do = (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = bd.sparse_attn_fwd(lay, q, k, v)
+    dq, dk, dv = bd.sparse_attn_bwd(lay, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    for h, head in enumerate(heads):
+        args = (head.kind, n, head.l)
+        rows = [0, 1, 17, n // 2, (1 << 24) + 5, n - 65, n - 2, n - 1]
+        keys = [0, 5, n - 40, n - 17, n - 1]
+        rkeys = {i: OM.row_keys(head.kind, i, n, head.l) for i in rows}
+        seers = {j: OM.rows_seeing(head.kind, j, n, head.l) for j in keys}
+        skeys = {int(i): OM.row_keys(head.kind, int(i), n, head.l) for j in keys for i in seers[j]}
+        u, m = _compact([rows, keys, *rkeys.values(), *seers.values(), *skeys.values()])
+        ut = torch.from_numpy(u).to(dev)
+        qc, kc, vc, doc = (to64(t[0, h].index_select(0, ut)) for t in (q, k, v, do))
+        kf = lambda ic: m(OM.row_keys(head.kind, int(u[ic]), n, head.l))
+        rf = lambda jc: m(OM.rows_seeing(head.kind, int(u[jc]), n, head.l))
+        rc, kc_ids = m(rows), m(keys)
+        ro, rl = OA.fwd_rows(qc, kc, vc, kf, rc)
+        rdq = OA.bwd_rows_dq(qc, kc, vc, doc, kf, rc)
+        rdk, rdv = OA.bwd_keys_dkdv(qc, kc, vc, doc, kf, rf, kc_ids)
+        ri, ki = torch.tensor(rows, device=dev), torch.tensor(keys, device=dev)
+        tag = f"n={n} h{h} {head.kind}"
+        assert_close(f"O {tag}", to64(o[0, h].index_select(0, ri)), ro, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
+        assert_close(f"LSE {tag}", to64(lse[0, h].index_select(0, ri)), rl, LSE_ABS)
+        assert_close(f"dQ {tag}", to64(dq[0, h].index_select(0, ri)), rdq, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
+        assert_close(f"dK {tag}", to64(dk[0, h].index_select(0, ki)), rdk, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
+        assert_close(f"dV {tag}", to64(dv[0, h].index_select(0, ki)), rdv, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
+        # every row: sum_j dK_j = 0 (scores are shift-invariant in the keys),
+        # sum_j dV_j = sum_i dO_i (probability rows sum to one)
+        sk = dk[0, h].float().sum(0)
+        assert float(sk.abs().max()) <= 2e-2 * float(dk[0, h].float().abs().sum(0).max()) + 1e-3
+        sv, sd = dv[0, h].float().sum(0), do[0, h].float().sum(0)
+        assert float((sv - sd).abs().max()) <= 1e-2 * float(dv[0, h].float().abs().sum(0).max()) + 1e-2
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
