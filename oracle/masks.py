@@ -186,24 +186,20 @@ def rows_seeing(kind: str, j: int, n: int, l: int, c: int | None = None,
 
 
 def local_global_mask(n: int, window: int, global_tokens=(0,)) -> np.ndarray:
-    """Causal sliding window plus global tokens (blog post on sliding windows, sections 03, 04, 07).
+    """Causal sliding window plus global tokens, as a set per query row.
 
-    A query reads key j when 0 <= i - j <= window, or when j is a global token
-    and j <= i; a global query still obeys causality and reads every j <= i.
+    Blog post on sliding windows, sections 03 and 04: query i reads key j iff
+    j <= i and at least one of (a) i - j <= window (the causal window),
+    (b) j is a global token, (c) i is a global token (a global query reads
+    its whole causal history).  Section 07 states the argument checks
+    (length > 0, window >= 0).
     """
     if not (n > 0 and window >= 0):
         raise ValueError("need n > 0 and window >= 0")
-    i = np.arange(n, dtype=np.int64)[:, None]
-    j = np.arange(n, dtype=np.int64)[None, :]
-    m = (j <= i) & (i - j <= window)
-    is_global = np.zeros(n, dtype=bool)
-    is_global[list(global_tokens)] = True
-    m |= is_global[None, :] & (j <= i)
-    for g in global_tokens:
-        m[g] = j[0] <= g
-    return m
-
-
-def pair_count(mask: np.ndarray) -> int:
-    """Number of allowed (query, key) pairs of a dense mask."""
-    return int(np.count_nonzero(mask))
+    g = np.unique(np.asarray(list(global_tokens), dtype=np.int64))
+    if g.size and (g[0] < 0 or g[-1] >= n):
+        raise ValueError("global tokens must lie in [0, n)")
+    pos = np.arange(n, dtype=np.int64)
+    in_g = np.isin(pos, g)
+    i, j = pos[:, None], pos[None, :]
+    return (j <= i) & ((i - j <= window) | in_g[None, :] | in_g[:, None])

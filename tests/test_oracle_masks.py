@@ -57,6 +57,22 @@ def test_local_global_worked_example(golden_dir):
     assert got.sum() == 26
 
 
+def test_local_global_mask_global_token_in_the_middle():
+    """Blog post on sliding windows, sections 03-04, worked by hand for a global
+    token that is not the first one: n = 6, window 1, G = {3}.  Row 3 is a global
+    query (its whole causal history); rows 4 and 5 add key 3 to their windows;
+    rows before 3 cannot read it (causality)."""
+    expect = {0: [0], 1: [0, 1], 2: [1, 2], 3: [0, 1, 2, 3], 4: [3, 4], 5: [3, 4, 5]}
+    got = M.local_global_mask(6, 1, (3,))
+    for i, keys in expect.items():
+        assert np.flatnonzero(got[i]).tolist() == keys, i
+    # Two global tokens, one of them past a row: window 0 (only itself), G = {1, 4}.
+    got = M.local_global_mask(6, 0, (1, 4))
+    assert [np.flatnonzero(r).tolist() for r in got] == [[0], [0, 1], [1, 2], [1, 3], [0, 1, 2, 3, 4], [1, 4, 5]]
+    with pytest.raises(ValueError):
+        M.local_global_mask(6, 1, (6,))
+
+
 def test_local_global_rejects_bad_args():
     """Section 07 asserts length > 0 and window >= 0."""
     with pytest.raises(ValueError):
