@@ -33,8 +33,9 @@ SA_XCDS = 8
 EXPORTED = (
     "sparse_attn_layout", "sparse_attn_layout_check", "sparse_attn_fwd_workspace",
     "sparse_attn_fwd", "sparse_attn_fwd_phases", "sparse_attn_bwd_workspace",
-    "sparse_attn_bwd", "sparse_attn_bwd_phases", "sparse_attn_strerror",
+    "sparse_attn_bwd", "sparse_attn_bwd_phases", "sparse_attn_bwd_static", "sparse_attn_strerror",
 )
+SA_STATIC_SCRATCH_BYTES = 64 << 20  # sparse_attn.h: device array of sparse_attn_bwd_static
 SA_FWD_MAIN, SA_FWD_MERGE, SA_FWD_ALL = 1, 2, 3
 SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_MERGE, SA_BWD_ALL = 1, 2, 4, 7
 SA_SCHED_FIELDS = 9
@@ -132,6 +133,9 @@ def load_library():
         lib.sparse_attn_bwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                                vp, vp, vp, sz, f32, ctypes.c_uint, vp]
         lib.sparse_attn_bwd_phases.restype = i32
+        lib.sparse_attn_bwd_static.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, f32, vp]
+        lib.sparse_attn_bwd_static.restype = i32
         lib.sparse_attn_strerror.argtypes = [i32]
         lib.sparse_attn_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -430,4 +434,33 @@ def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = N
     else:
         rc = lib.sparse_attn_bwd_phases(*args, phases, stream)
     _check(rc, "sparse_attn_bwd")
+    return dq, dk, dv
+
+
+def sparse_attn_bwd_static(layout: Layout, q, k, v, o, lse, do, scale: float | None = None,
+                           grads=None):
+    """Backward through the allocation-free entry point (``sparse_attn_bwd_static``):
+    the library's own per-GPU device array serves as workspace.  Returns
+    (dq, dk, dv); pass ``grads`` to write into existing tensors (then nothing
+    is allocated by this call either).  Calls on one GPU must not overlap."""
+    import torch
+    lib = load_library()
+    B, H, n, d, dt = _check_qkv(layout, (q, k, v, o, do), ("q", "k", "v", "o", "do"))
+    _check_lse(lse, B, H, n, q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_like(t, q, nm)
+    blob_dev = layout.device_blob(q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.sparse_attn_bwd_static(layout.blob.ctypes.data, _ptr(blob_dev), B, H, d, dt,
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                    _ptr(dq), _ptr(dk), _ptr(dv),
+                                    0.0 if scale is None else float(scale), stream)
+    if rc == SA_ESIZE:
+        need = bwd_workspace_bytes(layout, B, H, d, dt)
+        raise SparseAttnError(rc, f"sparse_attn_bwd_static: these sizes need {need} bytes of "
+                                  f"workspace, the static array holds {SA_STATIC_SCRATCH_BYTES}")
+    _check(rc, "sparse_attn_bwd_static")
     return dq, dk, dv

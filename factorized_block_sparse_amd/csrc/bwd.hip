@@ -858,3 +858,58 @@ extern "C" int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int 
   return sparse_attn_bwd_phases(blob_host, blob_dev, B, H, d, dtype, q, k, v, o, lse, dO, dq, dk,
                                 dv, workspace, ws_bytes, scale, SA_BWD_ALL, stream);
 }
+
+// --------------------------------------------------------------------------
+// Allocation-free backward: the workspace is a file-scope device array of
+// SA_STATIC_SCRATCH_BYTES, one copy per GPU, held until the process ends.
+// --------------------------------------------------------------------------
+#include <mutex>
+
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[SA_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each GPU, resolved once per device with that
+// device current (the host-side name `scratch` is not a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int static_scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return SA_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return SA_EHIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_bwd_static(const void* blob_host, const void* blob_dev, int B, int H,
+                                      int d, int dtype, const void* q, const void* k,
+                                      const void* v, const void* o, const float* lse,
+                                      const void* dO, void* dq, void* dk, void* dv, float scale,
+                                      void* stream) {
+  size_t need = 0;
+  int rc = sparse_attn_bwd_workspace(blob_host, B, H, d, dtype, &need);
+  if (rc != SA_OK) return rc;
+  if (need > size_t(SA_STATIC_SCRATCH_BYTES)) return SA_ESIZE;
+  void* ws = nullptr;
+  if (B > 0) {
+    rc = static_scratch_address(&ws);
+    if (rc != SA_OK) return rc;
+  }
+  return sparse_attn_bwd_phases(blob_host, blob_dev, B, H, d, dtype, q, k, v, o, lse, dO, dq, dk,
+                                dv, ws, size_t(SA_STATIC_SCRATCH_BYTES), scale, SA_BWD_ALL, stream);
+}

@@ -46,9 +46,10 @@
  *     Calls enqueue work and return without synchronising.
  *
  * Ownership.  The caller owns every buffer.  The library allocates and frees
- * no device memory and keeps no global mutable state: the layout blob is an
- * immutable, position-independent byte array that may be shared across
- * streams and calls.
+ * no device memory and keeps no global mutable state, with one exception:
+ * sparse_attn_bwd_static works in a file-scope device array of its own (one
+ * per GPU, see there).  The layout blob is an immutable, position-independent
+ * byte array that may be shared across streams and calls.
  *
  * Errors.  Every function returns SA_OK (0) or a negative status and never
  * aborts.  Arguments are validated before anything is enqueued, so an error
@@ -328,6 +329,25 @@ int sparse_attn_bwd_phases(const void* blob_host, const void* blob_dev, int B, i
                            const float* lse, const void* dO, void* dq, void* dk, void* dv,
                            void* workspace, size_t ws_bytes, float scale, unsigned phases,
                            void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * (code under stream capture, serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as sparse_attn_bwd, without the
+ * workspace: the library uses a file-scope device array of
+ * SA_STATIC_SCRATCH_BYTES instead, one per GPU, held from the library's first
+ * use on that GPU until the process ends.  Its device address is looked up
+ * once per GPU (the current device of the first call).  Returns SA_ESIZE,
+ * before any work is enqueued, when these sizes need more workspace than
+ * that (sparse_attn_bwd_workspace tells how much).  Calls allocate and free
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; the array keeps the previous call's contents,
+ * which the backward never reads before writing. */
+#define SA_STATIC_SCRATCH_BYTES (64u << 20)
+int sparse_attn_bwd_static(const void* blob_host, const void* blob_dev, int B, int H, int d,
+                           int dtype, const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                           float scale, void* stream);
 
 /* Static description of a status code. */
 const char* sparse_attn_strerror(int status);

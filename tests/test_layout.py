@@ -486,6 +486,24 @@ def test_fwd_bwd_argument_errors_before_any_launch():
                           + rnd(3 * hdr.num_qslots * 64 * 64 * 4))
 
 
+def test_static_backward_checks_before_any_launch():
+    """sparse_attn_bwd_static validates like sparse_attn_bwd and refuses sizes past its
+    static array with SA_ESIZE before touching the device (runs without a GPU)."""
+    lib = bd.load_library()
+    lay = Layout(4096, [HeadPattern("local", 8), HeadPattern("stride", 8)], 64, 64)
+    hb = lay.blob.ctypes.data
+    fake = 1 << 20
+    s = lambda B, H=2, d=64, dt=0, blob=hb: lib.sparse_attn_bwd_static(
+        blob, fake, B, H, d, dt, fake, fake, fake, fake, fake, fake, fake, fake, fake, 0.0, None)
+    big_b = bd.SA_STATIC_SCRATCH_BYTES // (2 * 4096 * 4) + 1  # D alone overflows the array
+    assert s(big_b) == bd.SA_ESIZE
+    assert s(1, blob=None) == bd.SA_EINVAL
+    assert s(1, H=3) == bd.SA_EINVAL
+    assert s(1, d=128) == bd.SA_EUNSUPPORTED
+    assert s(1, dt=1) == bd.SA_EUNSUPPORTED
+    assert s(0) == bd.SA_OK  # empty batch: nothing to do, no device lookup
+
+
 def test_profile_summaries_parse_and_track_the_sources(tmp_path):
     """The committed counter summary lists the bench kernels; a summary whose source hash
     differs from the current kernels is ignored (its traffic would describe other code)."""
