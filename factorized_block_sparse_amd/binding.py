@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsparse_attn.so"
 
 # enum values of sparse_attn.h
-SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ESIZE, SA_EHIP = 0, -1, -2, -3, -4
+SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ESIZE, SA_EHIP, SA_ENOMEM = 0, -1, -2, -3, -4, -5
 KINDS = {"local": 0, "stride": 1, "sameblock": 2, "summary": 3, "fixed_merged": 4,
          "local_global": 5, "strided_merged": 6}
 SA_STRIDE_FAR = 7  # blob-only pattern kind: second part of a merged strided head

@@ -38,6 +38,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <new>
 #include <tuple>
 #include <vector>
 
@@ -220,7 +221,30 @@ int build_maps(Pattern& P, int64_t n64, int32_t n_pad, bool self_if_empty) {
   return SA_OK;
 }
 
-void build_tiles(Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
+// An upper bound on the active tiles of a pattern, from each query tile's
+// widest key interval and longest prefix (no tile is touched outside them).
+int64_t tile_bound(const Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
+  const int32_t nqt = n_pad / bq, nkt = n_pad / bk;
+  int64_t bound = 0;
+  for (int32_t qt = 0; qt < nqt; ++qt) {
+    int32_t lo = INT32_MAX, hi = -1, pre = 0;
+    for (int32_t r = qt * bq; r < std::min(qt * bq + bq, n); ++r) {
+      if (P.lo[r] <= P.hi[r]) {
+        lo = std::min(lo, P.lo[r]);
+        hi = std::max(hi, P.hi[r]);
+      }
+      if (!P.pre.empty()) pre = std::max(pre, P.pre[r]);
+    }
+    int64_t t = (hi >= lo ? int64_t(hi / bk - lo / bk + 1) : 0) + (pre + bk - 1) / bk;
+    bound += std::min<int64_t>(t, nkt);
+  }
+  return bound;
+}
+
+// CSR / CSC arrays are indexed with int32: layouts whose active tiles could
+// exceed that range are refused (SA_EUNSUPPORTED) before they are built.
+int build_tiles(Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
+  if (tile_bound(P, n, n_pad, bq, bk) > int64_t(INT32_MAX)) return SA_EUNSUPPORTED;
   const int32_t nqt = n_pad / bq, nkt = n_pad / bk;
   P.row_ptr.assign(nqt + 1, 0);
   P.col.clear();
@@ -284,6 +308,7 @@ void build_tiles(Pattern& P, int32_t n, int32_t n_pad, int32_t bq, int32_t bk) {
       P.bflag[dst] = P.fflag[e];
     }
   }
+  return SA_OK;
 }
 
 int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
@@ -392,7 +417,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
       P.p = c;
       const int rc2 = build_maps(P, n, n_pad, self_if_empty);
       if (rc2 != SA_OK) return rc2;
-      build_tiles(P, n, n_pad, bq, bk);
+      const int rc3 = build_tiles(P, n, n_pad, bq, bk);
+      if (rc3 != SA_OK) return rc3;
       it = index.emplace(key, int32_t(pats.size())).first;
       pats.push_back(std::move(P));
     }
@@ -659,8 +685,10 @@ bool in_blob(int64_t off, int64_t bytes, int64_t total) {
 extern "C" int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_bytes) {
   try {
     return build(desc, static_cast<uint8_t*>(blob), blob_bytes);
+  } catch (const std::bad_alloc&) {
+    return SA_ENOMEM;  // host memory for the build ran out: never throw across the ABI
   } catch (...) {
-    return SA_EINVAL;  // allocation failure or similar: never throw across the ABI
+    return SA_EINVAL;
   }
 }
 
@@ -733,6 +761,7 @@ extern "C" const char* sparse_attn_strerror(int status) {
     case SA_EUNSUPPORTED: return "unsupported configuration";
     case SA_ESIZE: return "buffer too small";
     case SA_EHIP: return "HIP runtime error";
+    case SA_ENOMEM: return "out of host memory";
     default: return "unknown status";
   }
 }

@@ -71,7 +71,8 @@ enum sa_status {
   SA_EINVAL = -1,        /* malformed argument: NULL/misaligned pointer, bad size or pattern */
   SA_EUNSUPPORTED = -2,  /* well-formed but not implemented: d != 64, dtype, tile shape */
   SA_ESIZE = -3,         /* a caller buffer is too small (blob or workspace) */
-  SA_EHIP = -4           /* the HIP runtime reported an error at launch */
+  SA_EHIP = -4,          /* the HIP runtime reported an error at launch */
+  SA_ENOMEM = -5         /* the layout build ran out of host memory */
 };
 
 enum sa_head_kind {
@@ -251,7 +252,9 @@ typedef struct {
 
 /* Build the layout.  With blob == NULL, only *blob_bytes is set (size query).
  * Otherwise *blob_bytes must hold the blob's capacity (SA_ESIZE if too small)
- * and is set to the bytes written.  Host-only; needs no GPU. */
+ * and is set to the bytes written.  Host-only; needs no GPU.  A pattern whose
+ * active tiles could exceed INT32_MAX (the CSR / CSC index range) is refused
+ * with SA_EUNSUPPORTED; SA_ENOMEM when host memory for the build runs out. */
 int sparse_attn_layout(const sa_layout_desc* desc, void* blob, size_t* blob_bytes);
 
 /* Check a blob's header and internal offsets (host). */

@@ -1,8 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Small cases compare every element (several tiles, ragged tails, every head
-kind, all tile shapes).  Full-size workloads compare sampled rows and keys
-that the oracle computes one by one, plus invariants that hold at any size.
+kind, all tile shapes).  The longest sequence the kernels address compares
+sampled rows and keys that the oracle computes one by one, plus invariants
+that hold at any size.
 """
 
 import zlib
@@ -71,6 +72,13 @@ SMALL = [
     ("strided_merged_q128_k64", 1, 640, 128, 64, [HeadPattern("strided_merged", 40)]),
     ("split_strided_merged", 1, 2300, 64, 64, [HeadPattern("strided_merged", 1100),
                                                HeadPattern("strided_merged", 16)], 512),
+    # 128-row query tiles over 32-key tiles (one-wave dK/dV workgroups in two 64-row steps)
+    ("tiles128x32", 1, 400, 128, 32, [HeadPattern("local", 40), HeadPattern("stride", 40),
+                                      HeadPattern("sameblock", 50), HeadPattern("summary", 64, 8, 1),
+                                      HeadPattern("fixed_merged", 32, 4, 2), HeadPattern("strided_merged", 9),
+                                      HeadPattern("local_global", 30, 7)]),
+    ("split_tiles128x32", 2, 2200, 128, 32, [HeadPattern("local", 2100), HeadPattern("summary", 64, 32, 0),
+                                             HeadPattern("fixed_merged", 64, 16, 1)], 1024),
     # 128-key tiles (four waves of 32 keys in the dK/dV pass)
     ("fixed_tiles128", 1, 768, 128, 128, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
                                           HeadPattern("summary", 128, 32, 3), HeadPattern("local", 100)]),
@@ -129,6 +137,21 @@ def test_fp32_forward_split_rows():
     assert lay.header.comb_sched_len > 0
     inp = W.make_inputs(1, 2, 1100, 64, seed=6, dtype="fp32")
     _check_dense(lay, heads, 1, 1100, inp, backward=False, fp32=True)
+
+
+def test_fp32_forward_query_tiles128():
+    """float32 forward with 128-row query tiles (four waves), ragged and split."""
+    heads = [HeadPattern("local", 9), HeadPattern("stride", 9), HeadPattern("summary", 9, 3, 0),
+             HeadPattern("sameblock", 100), HeadPattern("fixed_merged", 20, 4, 1),
+             HeadPattern("local_global", 12, 5)]
+    lay = Layout(333, heads, 128, 32)
+    inp = W.make_inputs(2, len(heads), 333, 64, seed=15, dtype="fp32")
+    _check_dense(lay, heads, 2, 333, inp, backward=False, fp32=True)
+    heads = [HeadPattern("local", 1300), HeadPattern("summary", 64, 16, 2)]
+    lay = Layout(1400, heads, 128, 32, split_keys=512)
+    assert lay.header.comb_sched_len > 0
+    inp = W.make_inputs(1, 2, 1400, 64, seed=16, dtype="fp32")
+    _check_dense(lay, heads, 1, 1400, inp, backward=False, fp32=True)
 
 
 def test_workload_strided_n1024_fp32_full():
@@ -248,64 +271,9 @@ def test_masked_value_perturbation_on_gpu():
 
 
 # ----------------------------------------------------------------------------
-# Full-size workloads: sampled rows / keys + invariants
+# The longest sequence: sampled rows / keys + invariants (every element of the
+# full-size workloads is in test_gpu_full_size.py)
 # ----------------------------------------------------------------------------
-
-def _sample_rows(n, l, rng, extra=6):
-    base = {0, 1, l - 1, l, 2 * l + 3, n // 2, n - 2, n - 1, 95, 96, 127, 128}
-    base |= set(rng.integers(0, n, extra).tolist())
-    return sorted(r for r in base if 0 <= r < n)
-
-
-@pytest.mark.parametrize("wname", ["strided_n12288", "fixed_n12288", "fixed_c8_n12288", "strided_n65536",
-                                   "fixed_merged_n12288", "local_global_n12288",
-                                   "strided_merged_n12288"])
-def test_workload_full_size_sampled(wname):
-    w = W.WORKLOADS[wname]
-    lay = Layout(w.n, w.heads, w.block_q, w.block_k)
-    inp = W.workload_inputs(w)
-    out = run_gpu(lay, inp, True)
-    rng = np.random.default_rng(2024)
-    q, k, v, do = (to64(inp[x]) for x in ("q", "k", "v", "do"))
-    heads_to_check = range(w.H) if w.H <= 4 else sorted({0, 1, 2, 3, w.H - 2, w.H - 1})
-    for b in range(w.B):
-        for h in (heads_to_check if b == 0 else (0, 1)):
-            head = w.heads[h]
-            kf = OA.keys_fn_for(head.kind, w.n, head.l, head.c or None, head.sub)
-            rf = OA.rows_seeing_fn_for(head.kind, w.n, head.l, head.c or None, head.sub)
-            rows = _sample_rows(w.n, head.l, rng)
-            o, lse = OA.fwd_rows(q[b, h], k[b, h], v[b, h], kf, rows)
-            tag = f"{wname} b{b} h{h} {head.kind}"
-            assert_close(f"O {tag}", out["o"][b, h][rows], o, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
-            assert_close(f"LSE {tag}", out["lse"][b, h][rows], lse, LSE_ABS)
-            dq = OA.bwd_rows_dq(q[b, h], k[b, h], v[b, h], do[b, h], kf, rows)
-            assert_close(f"dQ {tag}", out["dq"][b, h][rows], dq, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
-            if head.kind == "summary":
-                s = OM.summary_start(head.l, head.c, head.sub)
-                keys = [s, s + head.c - 1, w.n - head.l + s]         # summary cells
-                keys += [max(0, s - 1)] if s > 0 else []             # a self-if-empty key
-                cand = [head.l + (s + head.c) % head.l, w.n - 1, w.n - head.l + (s - 1) % head.l]
-                dead = [j for j in cand if rf(j).size == 0]
-                assert dead
-            else:
-                keys = sorted({0, 1, head.l, w.n // 3, w.n - 1, int(rng.integers(0, w.n))})
-                dead = []
-            dk, dv = OA.bwd_keys_dkdv(q[b, h], k[b, h], v[b, h], do[b, h], kf, rf, keys)
-            assert_close(f"dK {tag}", out["dk"][b, h][keys], dk, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
-            assert_close(f"dV {tag}", out["dv"][b, h][keys], dv, BF16_MAX_ABS, BF16_REL_RMS, bf16_output=True)
-            for j in dead:
-                assert (out["dk"][b, h][j] == 0).all() and (out["dv"][b, h][j] == 0).all()
-    # Invariants at full size for every (b, h): sum_j dK_j = 0, sum_j dV_j = sum_i dO_i.
-    for b in range(w.B):
-        for h in range(w.H):
-            sk = out["dk"][b, h].sum(0)
-            scale_k = np.abs(out["dk"][b, h]).sum(0).max() + 1e-30
-            assert np.max(np.abs(sk)) <= 2e-2 * scale_k + 1e-3, (b, h)
-            sv = out["dv"][b, h].sum(0)
-            ref = do[b, h].sum(0)
-            assert np.max(np.abs(sv - ref)) <= 1e-2 * np.abs(out["dv"][b, h]).sum(0).max() + 1e-2, (b, h)
-    assert np.isfinite(out["o"]).all() and np.isfinite(out["dq"]).all()
-
 
 def _compact(tokens):
     """Sorted token universe and a map from token arrays to indices into it."""

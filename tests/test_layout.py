@@ -43,7 +43,8 @@ def _doc_maps(kind, n, n_pad, l, c=0, sub=0):
         qmap[:n] = np.arange(n)
         cells = [j for j in range(n) if s <= j % l <= s + c - 1]
         empty = [i for i in range(n) if M.row_keys(M.SUMMARY, i, n, l, c, sub, self_if_empty=False).size == 0]
-        rest = [j for j in range(n) if j not in set(cells) | set(empty)]
+        taken = set(cells) | set(empty)
+        rest = [j for j in range(n) if j not in taken]
         kmap[:n] = cells + empty + rest
     return qmap, kmap
 
@@ -126,6 +127,89 @@ def test_layout_bit_exact(n, bq, bk, heads):
             np.testing.assert_array_equal(arr[name], r, err_msg=f"{head} {name}")
         assert rec.nnz == len(ref[1])
     assert lay.pairs_per_batch() == total_pairs
+
+
+def _check_pattern_from_rows(lay, pi, kind, n, keys_of, qmap, kmap, bq, bk, tag):
+    """One pattern of a built layout against a reference made from the oracle's
+    per-row key lists (no n x n mask): maps, per-token counts, each layout row
+    reading exactly its prefix and interval, active / FULL tiles, CSR and CSC."""
+    h = lay.header
+    n_pad, nqt, nkt = h.n_pad, h.nqt, h.nkt
+    arr, rec = lay.pattern_arrays(pi), lay.pattern_rec(pi)
+    np.testing.assert_array_equal(arr["qmap"], qmap, err_msg=f"{tag} qmap")
+    np.testing.assert_array_equal(arr["kmap"], kmap, err_msg=f"{tag} kmap")
+    kpos = np.empty(n, dtype=np.int64)
+    kpos[kmap[:n]] = np.arange(n)
+    count = np.zeros(n, dtype=np.int64)
+    tiles = np.zeros((nqt, nkt), dtype=np.int64)
+    lo, hi, pre = arr["lo"].astype(np.int64), arr["hi"].astype(np.int64), arr["pre"].astype(np.int64)
+    pairs = 0
+    for qt in range(nqt):
+        kts = []
+        for p in range(qt * bq, (qt + 1) * bq):
+            t = int(qmap[p])
+            if t < 0:
+                assert pre[p] == 0 and lo[p] > hi[p], f"{tag} padding row {p}"
+                continue
+            kp = np.sort(kpos[keys_of(t)])
+            count[t] = kp.size
+            pairs += kp.size
+            a, b, c0 = int(lo[p]), int(hi[p]), int(pre[p])
+            span = np.arange(a, b + 1) if a <= b else np.zeros(0, dtype=np.int64)
+            expect = np.concatenate([np.arange(c0), span])
+            assert kp.size == expect.size and (kp == expect).all(), f"{tag} row {p} (token {t})"
+            kts.append(kp // bk)
+        if kts:
+            tiles[qt] = np.bincount(np.concatenate(kts), minlength=nkt)
+    np.testing.assert_array_equal(arr["count"], count, err_msg=f"{tag} count")
+    assert rec.pairs == pairs and rec.kind == kind
+    active, full = tiles > 0, tiles == bq * bk
+    row_ptr = np.concatenate([[0], np.cumsum(active.sum(1))])
+    qi, ki = np.nonzero(active)
+    col_ptr = np.concatenate([[0], np.cumsum(active.sum(0))])
+    kj, qj = np.nonzero(active.T)
+    ref = {"row_ptr": row_ptr, "col": ki, "fflag": full[qi, ki], "col_ptr": col_ptr, "row": qj,
+           "bflag": full.T[kj, qj]}
+    for name, r in ref.items():
+        np.testing.assert_array_equal(arr[name], np.asarray(r).astype(arr[name].dtype),
+                                      err_msg=f"{tag} {name}")
+    assert rec.nnz == len(ki)
+
+
+@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+def test_workload_layouts_bit_exact_from_oracle_rows(wname):
+    """The layouts the benchmark and the full-size parity tests run, at their real n and
+    tiles (strided n = 3,072 on 64x64, fixed n = 12,288 on 128x128, strided n = 12,288
+    on 32x32, strided n = 65,536 on 64x64, and the union workloads), bit for bit
+    against tiles built from the oracle's row key lists."""
+    w = W.WORKLOADS[wname]
+    lay = Layout(w.n, w.heads, w.block_q, w.block_k)
+    h = lay.header
+    n, n_pad = w.n, h.n_pad
+    hp = lay.head_pattern_index()
+    part, _ = lay.head_parts()
+    seen = set()
+    for hi_, head in enumerate(w.heads):
+        c = head.c or None
+        if head.kind == "strided_merged":
+            # two parts with disjoint key sets: the local band, then the stride
+            # members at distance >= 2 l (residue-class order)
+            parts = [(int(hp[hi_]), bd.KINDS["local"], "local",
+                      lambda t, l=head.l: M.row_keys(M.LOCAL, t, n, l)),
+                     (int(part[hi_]), bd.SA_STRIDE_FAR, "stride",
+                      lambda t, l=head.l: np.setdiff1d(M.row_keys(M.STRIDE, t, n, l),
+                                                       M.row_keys(M.LOCAL, t, n, l)))]
+        else:
+            parts = [(int(hp[hi_]), bd.KINDS[head.kind], head.kind,
+                      lambda t, hd=head, c=c: M.row_keys(hd.kind, t, n, hd.l, c, hd.sub))]
+        for pi, kind, order, keys_of in parts:
+            if pi in seen:
+                continue
+            seen.add(pi)
+            qmap, kmap = _doc_maps(order, n, n_pad, head.l, head.c, head.sub)
+            _check_pattern_from_rows(lay, pi, kind, n, keys_of, qmap, kmap, w.block_q, w.block_k,
+                                     f"{wname} head {hi_} ({head.kind}) pattern {pi}")
+    assert len(seen) == h.num_patterns
 
 
 def test_patterns_are_shared_between_equal_heads():
@@ -484,6 +568,22 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert hdr.red_sched_len > 0 and hdr.comb_sched_len > 0
     assert size.value == (rnd(3 * 2 * 12288 * 4) + rnd(3 * hdr.num_slots * 2 * 64 * 64 * 4)
                           + rnd(3 * hdr.num_qslots * 64 * 64 * 4))
+
+
+def test_layout_refuses_tile_counts_past_int32():
+    """CSR / CSC entries are int32: a pattern whose active tiles could pass INT32_MAX
+    (a local band as long as n = 2^21 on 32 x 32 tiles: 65,536 * 65,537 / 2 tiles) is
+    refused by the size-only pass before anything is built."""
+    lib = bd.load_library()
+    n = 1 << 21
+    heads = (bd.CHeadPattern * 1)(bd.CHeadPattern(bd.KINDS["local"], n, 0, 0))
+    desc = bd.CLayoutDesc(n, 32, 32, 1, heads, bd.SA_SELF_IF_EMPTY, 0, 0)
+    size = ctypes.c_size_t(0)
+    assert lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)) == bd.SA_EUNSUPPORTED
+    # 64 x 64 tiles: a quarter of the tiles, within range (size query only)
+    desc = bd.CLayoutDesc(1 << 16, 64, 64, 1, heads, bd.SA_SELF_IF_EMPTY, 0, 0)
+    assert lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)) == bd.SA_OK
+    assert lib.sparse_attn_strerror(bd.SA_ENOMEM) == b"out of host memory"
 
 
 def test_static_backward_checks_before_any_launch():
