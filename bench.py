@@ -63,7 +63,7 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
     # query-tile pass; dV = P^T dO, dP = dO V^T and dK = dS^T Q (6 d) in the
     # key-tile pass.  Score recomputation is not counted.
     if label == "bwd_dq":
-        return 2 * D * pairs, rows * (5 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
+        return 2 * D * pairs, rows * (6 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
     if label == "bwd_dkdv":
         return 6 * D * pairs, rows * (6 * D * 2 + 8)             # Q,K,V,dO read, dK,dV write; LSE, D
     if label in ("fwd_merge", "bwd_merge"):
@@ -261,7 +261,8 @@ def _cpu_task(args):
     from oracle import attention as OA
     q, k, v, do, head, n = _CPU[key]
     kf = OA.keys_fn_for(head.kind, n, head.l, head.c or None, head.sub)
-    OA.bwd_rows_full(q, k, v, do, kf, rows=rows)
+    OA.fwd_rows(q, k, v, kf, rows)              # O, LSE: 4 d per key
+    OA.bwd_rows_full(q, k, v, do, kf, rows=rows)  # dV, dP, dQ, dK: 8 d per key
     fl = 0
     for i in rows:
         fl += 12 * D * kf(i).size
@@ -302,8 +303,9 @@ def cpu_baseline(workloads, inputs, seconds: float):
             "host_cpu": host_cpu_model(), "nproc": os.cpu_count(),
             "sample": (f"{rows_done} of the {total_rows} query rows of {'+'.join(w.name for w in workloads)} "
                        f"(random order over every batch element and head) through the float64 row-gather "
-                       f"oracle forward+backward in {wall:.1f} s of wall time (deadline {seconds:.0f} s); "
-                       f"useful FLOPs 12*d*keys per row"),
+                       f"oracle forward (fwd_rows) and backward (bwd_rows_full) in {wall:.1f} s of wall "
+                       f"time (deadline {seconds:.0f} s); useful FLOPs 12*d*keys per row (4 d forward, 8 d "
+                       f"backward)"),
             "seconds": wall}
 
 
@@ -355,6 +357,75 @@ def time_config(torch, bd, W, n: int, heads, block_q: int, block_k: int, B: int,
             "fwd_ms": round(fwd_ms, 4), "fwd_bwd_ms": round(both_ms, 4),
             "useful_tflops": round(useful / (both_ms * 1e-3) / 1e12, 2),
             "layout_build_ms": round(layout_ms, 2)}
+
+
+def time_workload(torch, bd, W, w, steps: int, warmup: int) -> dict:
+    """Forward and forward + backward ms of one named workload on its own inputs."""
+    lay = bd.Layout(w.n, w.heads, w.block_q, w.block_k)
+    inp = W.workload_inputs(w)
+    q, k, v, do = (inp[x].to("cuda") for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    fws = torch.empty(max(1, bd.fwd_workspace_bytes(lay, w.B, w.H)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(bd.bwd_workspace_bytes(lay, w.B, w.H), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws)
+
+    def both():
+        fwd()
+        bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    fwd_ms, both_ms = timed(fwd), timed(both)
+    pairs = lay.pairs_per_batch() * w.B
+    area = lay.tiles_per_batch() * w.B * w.block_q * w.block_k
+    return {"B": w.B, "H": w.H, "n": w.n, "tiles": [w.block_q, w.block_k], "pairs": pairs,
+            "tile_padding_overhead": round(area / pairs, 3), "fwd_ms": round(fwd_ms, 4),
+            "ms": round(both_ms, 4),
+            "useful_tflops": round(12 * D * pairs / (both_ms * 1e-3) / 1e12, 2),
+            "computed_over_dense_causal": round(area / (w.B * w.H * w.n * (w.n + 1) / 2), 4)}
+
+
+def scaling_report(torch, bd, W, names, runs, per_wl, steps: int, warmup: int) -> dict:
+    """The strided workloads at n = 3,072 and 65,536 beside the n = 12,288 one,
+    and the growth exponents of the strided pattern over n = 1,024 .. 65,536
+    (H = 8 alternating local / stride heads, l = 2^round(log2 sqrt n), 64 x 64
+    tiles; host-side layout counts)."""
+    out = {"workloads": {}}
+    for nm in names:
+        out["workloads"][nm] = time_workload(torch, bd, W, W.WORKLOADS[nm], steps, warmup)
+    ns = [1 << e for e in range(10, 17)]
+    lays = [bd.Layout(n, W.strided_heads(8, 1 << round(math.log2(math.sqrt(n)))), 64, 64) for n in ns]
+    out["exponent_pairs"] = round(fit_exponent(ns, [lay.pairs_per_batch() for lay in lays]), 3)
+    out["exponent_computed_tile_area"] = round(fit_exponent(ns, [lay.tiles_per_batch() for lay in lays]), 3)
+    # time per (batch, head) of the strided workloads against n
+    pts = {}
+    for nm, r in out["workloads"].items():
+        if nm.startswith("strided_n") and "fp32" not in nm:
+            pts[r["n"]] = r["ms"] / (r["B"] * r["H"])
+    for r in runs:
+        w = r["w"]
+        if w.name.startswith("strided_n") and w.name in per_wl:
+            pts[w.n] = per_wl[w.name]["ms"] / (w.B * w.H)
+    if len(pts) >= 2:
+        xs = sorted(pts)
+        out["exponent_time_per_head_strided"] = round(fit_exponent(xs, [pts[x] for x in xs]), 3)
+        out["time_per_head_ms"] = {str(x): round(pts[x], 5) for x in xs}
+    out["expected_exponent"] = 1.5
+    return out
 
 
 def fit_exponent(xs, ys) -> float:
@@ -490,6 +561,15 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the workloads, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, for scaling HBM byte counters)")
+    ap.add_argument("--preroll-ms", type=float, default=250.0,
+                    help="untimed steps for this long before the warm-up steps, so that clocks and "
+                         "caches settle whatever --warmup is (reported as preroll)")
+    ap.add_argument("--scaling-workloads", default="strided_n3072,strided_n65536",
+                    help="further workloads timed (forward and forward + backward) after the "
+                         "benchmark, reported under scaling; empty to skip")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the calibration micro-benchmarks (measured MFMA rate and clock, "
+                         "VALU and LDS rates, atomic throughput)")
     ap.add_argument("--sweep-n", action="store_true",
                     help="instead of the benchmark: the O(n sqrt n) sweep, one JSON line per n")
     ap.add_argument("--crossover", action="store_true",
@@ -571,6 +651,16 @@ def main():
         if evs is not None:
             evs[len(flat)].record()
 
+    # Pre-roll: untimed steps for a fixed wall time, then the W warm-up steps.
+    # Without it a short warm-up leaves the first timed steps slower than the
+    # steady state (clocks and caches still settling).
+    pre_steps, t_pre = 0, time.perf_counter()
+    while (time.perf_counter() - t_pre) * 1000.0 < args.preroll_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        pre_steps += 10
+    preroll = {"steps": pre_steps, "ms": round((time.perf_counter() - t_pre) * 1000.0, 1)}
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -660,6 +750,19 @@ def main():
     for k in kernels:
         k["ms"] = round(k["ms"], 4)
 
+    calibration = None
+    if not args.no_calibration:
+        try:
+            from factorized_block_sparse_amd import calibration as cal
+            calibration = cal.run()
+        except Exception as e:  # a reference only; never fails the bench
+            calibration = {"error": str(e)}
+
+    scaling = None
+    extra = [x for x in args.scaling_workloads.split(",") if x]
+    if extra:
+        scaling = scaling_report(torch, bd, W, extra, runs, per_wl, K, max(args.warmup, 5))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wls, inputs, args.cpu_seconds)
@@ -690,6 +793,9 @@ def main():
                                        "heads": sorted({h.kind for h in w.heads}),
                                        "tiles": [w.block_q, w.block_k]} for w in wls},
                    "per_workload": per_wl, "kernels": kernels},
+        "calibration": calibration,
+        "preroll": preroll,
+        "scaling": scaling,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_sources_sha256": kernel_sources_hash(),

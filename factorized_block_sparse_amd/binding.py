@@ -112,34 +112,38 @@ def load_library():
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{LIB_NAME} is not built ({path}); run `python -m factorized_block_sparse_amd.build`")
-        lib = ctypes.CDLL(path)
-        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        lib.sparse_attn_layout.argtypes = [ctypes.POINTER(CLayoutDesc), vp, ctypes.POINTER(sz)]
-        lib.sparse_attn_layout.restype = i32
-        lib.sparse_attn_layout_check.argtypes = [vp, sz]
-        lib.sparse_attn_layout_check.restype = i32
-        lib.sparse_attn_fwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
-        lib.sparse_attn_fwd_workspace.restype = i32
-        lib.sparse_attn_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, f32, vp]
-        lib.sparse_attn_fwd.restype = i32
-        lib.sparse_attn_fwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
-                                               f32, ctypes.c_uint, vp]
-        lib.sparse_attn_fwd_phases.restype = i32
-        lib.sparse_attn_bwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
-        lib.sparse_attn_bwd_workspace.restype = i32
-        lib.sparse_attn_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, sz, f32, vp]
-        lib.sparse_attn_bwd.restype = i32
-        lib.sparse_attn_bwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
-                                               vp, vp, vp, sz, f32, ctypes.c_uint, vp]
-        lib.sparse_attn_bwd_phases.restype = i32
-        lib.sparse_attn_bwd_static.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
-                                               vp, vp, vp, f32, vp]
-        lib.sparse_attn_bwd_static.restype = i32
-        lib.sparse_attn_strerror.argtypes = [i32]
-        lib.sparse_attn_strerror.restype = ctypes.c_char_p
-        _lib = lib
-        return lib
+        _lib = configure(ctypes.CDLL(path))
+        return _lib
+
+
+def configure(lib):
+    """Declare the argument and result types of the C ABI on a loaded library."""
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.sparse_attn_layout.argtypes = [ctypes.POINTER(CLayoutDesc), vp, ctypes.POINTER(sz)]
+    lib.sparse_attn_layout.restype = i32
+    lib.sparse_attn_layout_check.argtypes = [vp, sz]
+    lib.sparse_attn_layout_check.restype = i32
+    lib.sparse_attn_fwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.sparse_attn_fwd_workspace.restype = i32
+    lib.sparse_attn_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, f32, vp]
+    lib.sparse_attn_fwd.restype = i32
+    lib.sparse_attn_fwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
+                                           f32, ctypes.c_uint, vp]
+    lib.sparse_attn_fwd_phases.restype = i32
+    lib.sparse_attn_bwd_workspace.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.sparse_attn_bwd_workspace.restype = i32
+    lib.sparse_attn_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, sz, f32, vp]
+    lib.sparse_attn_bwd.restype = i32
+    lib.sparse_attn_bwd_phases.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, sz, f32, ctypes.c_uint, vp]
+    lib.sparse_attn_bwd_phases.restype = i32
+    lib.sparse_attn_bwd_static.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, f32, vp]
+    lib.sparse_attn_bwd_static.restype = i32
+    lib.sparse_attn_strerror.argtypes = [i32]
+    lib.sparse_attn_strerror.restype = ctypes.c_char_p
+    return lib
 
 
 def _strerror(status: int) -> str:

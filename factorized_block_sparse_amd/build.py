@@ -22,6 +22,10 @@ LIB_NAME = "libsparse_attn.so"
 ARCH = "gfx950"
 
 SOURCES = ["layout.cpp", "fwd.hip", "bwd.hip"]
+# Calibration micro-benchmarks (include/sa_probes.h), a library of their own:
+# the benchmark reads the measured ceilings from it; the attention path does not.
+PROBE_SOURCES = ["probes.hip"]
+PROBE_LIB_NAME = "libsa_probes.so"
 
 # Packed FP32 VALU ops are disabled for all device code: the kernels rely on
 # ordinary scalar float arithmetic only.
@@ -56,12 +60,8 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the shared library; returns its path."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    out = os.path.join(PKG, LIB_NAME)
+def _link(objs, name: str) -> str:
+    out = os.path.join(PKG, name)
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,6 +69,17 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link the attention library (returns its path)
+    and the calibration library beside it."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB_NAME)
+    return _link([objs[s] for s in SOURCES], LIB_NAME)
 
 
 if __name__ == "__main__":

@@ -80,3 +80,34 @@ def test_token_order_tile_area_matches_brute_force(n, l, c, sub, bq, bk):
     assert bench.natural_order_tile_area(n, head, bq, bk) == _brute_tile_area(n, OM.SUMMARY, l, c, sub, bq, bk)
     same = W.HeadSpec(W.SAMEBLOCK, l)
     assert bench.natural_order_tile_area(n, same, bq, bk) == _brute_tile_area(n, OM.SAMEBLOCK, l, None, 0, bq, bk)
+
+
+def test_kernel_bytes_count_every_tensor_the_kernel_moves():
+    """bwd_dq reads Q, K, V, O, dO and writes dQ (six rows of 64 bf16) plus LSE
+    and D; bwd_dkdv reads Q, K, V, dO and writes dK, dV (six rows) plus LSE and
+    D: 152.6 MB each at n = 12,288 with B * H = 16."""
+    rows = 2 * 8 * 12288
+    assert bench.kernel_work("bwd_dq", 2, 8, 12288, 1)[1] == rows * (6 * 64 * 2 + 8)
+    assert bench.kernel_work("bwd_dkdv", 2, 8, 12288, 1)[1] == rows * (6 * 64 * 2 + 8)
+    assert round(rows * 776 / 1e6, 1) == 152.6
+    assert bench.kernel_work("fwd", 2, 8, 12288, 1)[1] == rows * (4 * 64 * 2 + 4)
+
+
+def test_cpu_baseline_task_runs_what_it_counts(monkeypatch):
+    """The CPU leg counts 12 d FLOPs per visible key (4 d forward, 8 d backward),
+    so each task must run both the oracle's forward and its backward."""
+    import time
+    from oracle import attention as OA
+    calls = []
+    real_f, real_b = OA.fwd_rows, OA.bwd_rows_full
+    monkeypatch.setattr(OA, "fwd_rows", lambda *a, **k: calls.append("fwd") or real_f(*a, **k))
+    monkeypatch.setattr(OA, "bwd_rows_full", lambda *a, **k: calls.append("bwd") or real_b(*a, **k))
+    n = 64
+    rng = np.random.default_rng(0)
+    q, k, v, do = (rng.standard_normal((n, 64)) for _ in range(4))
+    head = W.HeadSpec(W.LOCAL, 5)
+    bench._CPU[("t", 0, 0)] = (q, k, v, do, head, n)
+    rows = [0, 3, 40]
+    done, fl = bench._cpu_task((("t", 0, 0), rows, time.time() + 60))
+    assert sorted(calls) == ["bwd", "fwd"] and done == 3
+    assert fl == 12 * 64 * sum(OM.row_keys(OM.LOCAL, i, n, 5).size for i in rows)
