@@ -480,6 +480,21 @@ def test_library_exports_every_declared_symbol():
     assert lib.sparse_attn_strerror(99) == b"unknown status"
 
 
+def test_probe_library_exports_its_header():
+    """The calibration library exports what include/sa_probes.h declares, and the
+    ctypes result struct matches the C one (loaded without a GPU: nothing runs)."""
+    import re
+    from factorized_block_sparse_amd import calibration as cal
+    text = open(os.path.join(ROOT, "include", "sa_probes.h")).read()
+    declared = set(re.findall(r"\b(sa_probe_[a-z_]+)\s*\(", text))
+    assert declared == {"sa_probe_run"}
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(bd.library_path()), cal.LIB_NAME))
+    assert all(hasattr(lib, nm) for nm in declared)
+    fields = re.findall(r"double\s+(\w+);", text)
+    assert tuple(fields) == cal.FIELDS
+    assert ctypes.sizeof(cal.ProbeResults) == 8 * len(fields)
+
+
 def test_ctypes_structs_match_the_c_header():
     """Sizes and offsets of the ABI structs, from a C compiler reading the header."""
     src = r"""
