@@ -224,10 +224,12 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     }
     const int k0 = kt * BK;
     const bool mine = ((lo <= hi) && (lo <= k0 + BK - 1) && (hi >= k0)) || (PRE && pre > k0);
-    // One tile; IS_FULL is a compile-time copy of the tile's FULL flag so the
-    // element loops carry no branch.
-    auto tile = [&](auto full_tag) {
-      constexpr bool IS_FULL = decltype(full_tag)::value;
+    // One tile; MASK is a compile-time copy of the tile's mask kind so the
+    // element loops carry no branch: 0 FULL (no mask), 1 every row's visible
+    // keys in the tile end at one bound (up_rel), 2 prefix and interval.
+    const int up = lo <= hi ? hi : pre - 1;
+    auto tile = [&](auto mask_tag) {
+      constexpr int MASK = decltype(mask_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         floatx16 s = floatx16{}, dp = ndv;  // dp accumulates dP - D
@@ -240,15 +242,14 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
         }
         // Register r of half g: key k0 + 32*kb + kappa(r, g); lane = query.
         const int lo_rel = lo - k0 - 32 * kb - 8 * g, hi_rel = hi - k0 - 32 * kb - 8 * g;
-        const int pre_rel = pre - k0 - 32 * kb - 8 * g;
+        const int pre_rel = pre - k0 - 32 * kb - 8 * g, up_rel = up - k0 - 32 * kb - 8 * g;
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fast_exp2(fmaf(s[r], c2, -lse2));
-          if (!IS_FULL) {
-            const int cr = 16 * (r >> 3) + (r & 7);  // key offset beyond 32*kb + 8*g
-            pr = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? pr : 0.f;
-          }
+          const int cr = 16 * (r >> 3) + (r & 7);  // key offset beyond 32*kb + 8*g
+          if (MASK == 1) pr = cr <= up_rel ? pr : 0.f;
+          if (MASK == 2) pr = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? pr : 0.f;
           ds[r] = pr * dp[r];
         }
 #pragma unroll
@@ -263,9 +264,11 @@ __global__ __launch_bounds__(BQ * 2, (BQ == 32 && BK == 64) ? 1 : 2) void bwd_dq
     };
     if (__any(mine)) {
       if (full)
-        tile(std::true_type{});
+        tile(std::integral_constant<int, 0>{});
+      else if (__all(lo > hi || lo <= k0))  // see the forward: one bound per row
+        tile(std::integral_constant<int, 1>{});
       else
-        tile(std::false_type{});
+        tile(std::integral_constant<int, 2>{});
     }
     wait_vmem();  // tile it+1 is in LDS (this wave's part)
     __syncthreads();

@@ -300,14 +300,29 @@ void fwd_bf16_kernel(FwdParams p) {
       if (!full) {
         // Key k0 + c is visible iff k0 + c < pre or lo <= k0 + c <= hi;
         // c = 32*kb + kappa(r, g) = 8*g + (a constant per register).
-        const int lo_rel = lo - k0 - 8 * g, hi_rel = hi - k0 - 8 * g, pre_rel = pre - k0 - 8 * g;
+        if (__all(lo > hi || lo <= k0)) {
+          // Every row's visible keys in this tile end at one bound (the usual
+          // causal diagonal): hi when its interval starts at or before the
+          // tile (a prefix ends before the interval), pre - 1 when the
+          // interval is empty.  One compare per score.
+          const int up_rel = (lo <= hi ? hi : pre - 1) - k0 - 8 * g;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int cr = 32 * kb + 16 * (r >> 3) + (r & 7);
-            s[kb][r] = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? s[kb][r] : -INFINITY;
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int cr = 32 * kb + 16 * (r >> 3) + (r & 7);
+              s[kb][r] = cr <= up_rel ? s[kb][r] : -INFINITY;
+            }
+        } else {
+          const int lo_rel = lo - k0 - 8 * g, hi_rel = hi - k0 - 8 * g, pre_rel = pre - k0 - 8 * g;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int cr = 32 * kb + 16 * (r >> 3) + (r & 7);
+              s[kb][r] = ((PRE && cr < pre_rel) || (cr >= lo_rel && cr <= hi_rel)) ? s[kb][r] : -INFINITY;
+            }
+        }
       }
       float mx = -INFINITY;  // max of the raw scores (scale > 0)
 #pragma unroll
