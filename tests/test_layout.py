@@ -212,6 +212,68 @@ def test_workload_layouts_bit_exact_from_oracle_rows(wname):
     assert len(seen) == h.num_patterns
 
 
+def _random_heads(rng, n_heads):
+    heads = []
+    for _ in range(n_heads):
+        kind = str(rng.choice(["local", "stride", "sameblock", "summary", "fixed_merged", "local_global",
+                               "strided_merged"]))
+        l = int(rng.integers(1, 80))
+        if kind in ("summary", "fixed_merged"):
+            c = int(rng.integers(1, l + 1))
+            heads.append(HeadPattern(kind, l, c, int(rng.integers(0, 6))))
+        elif kind == "local_global":
+            heads.append(HeadPattern(kind, l, int(rng.integers(0, 40))))
+        else:
+            heads.append(HeadPattern(kind, l))
+    return heads
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_layouts_bit_exact(seed):
+    """Seeded random layouts (any n up to 700, every head kind with random l, c and
+    sub-block, every tile shape the builder accepts): bit for bit against tiles
+    built from the oracle's row key lists, like the workload layouts."""
+    rng = np.random.default_rng(7000 + seed)
+    n = int(rng.integers(1, 701))
+    bq, bk = [(32, 32), (32, 64), (64, 32), (64, 64), (128, 32), (128, 64), (128, 128)][seed % 7]
+    heads = _random_heads(rng, int(rng.integers(1, 5)))
+    lay = Layout(n, heads, bq, bk, split_keys=int(rng.integers(32, 2048)),
+                 split_rows=int(rng.integers(32, 2048)))
+    h = lay.header
+    hp = lay.head_pattern_index()
+    part, _ = lay.head_parts()
+    seen = set()
+    for hi_, head in enumerate(heads):
+        c = head.c or None
+        if head.kind == "strided_merged":
+            parts = [(int(hp[hi_]), bd.KINDS["local"], "local",
+                      lambda t, l=head.l: M.row_keys(M.LOCAL, t, n, l)),
+                     (int(part[hi_]), bd.SA_STRIDE_FAR, "stride",
+                      lambda t, l=head.l: np.setdiff1d(M.row_keys(M.STRIDE, t, n, l),
+                                                       M.row_keys(M.LOCAL, t, n, l)))]
+        else:
+            parts = [(int(hp[hi_]), bd.KINDS[head.kind], head.kind,
+                      lambda t, hd=head, c=c: M.row_keys(hd.kind, t, n, hd.l, c, hd.sub))]
+        for pi, kind, order, keys_of in parts:
+            if pi in seen:
+                continue
+            seen.add(pi)
+            qmap, kmap = _doc_maps(order, n, h.n_pad, head.l, head.c, head.sub)
+            _check_pattern_from_rows(lay, pi, kind, n, keys_of, qmap, kmap, bq, bk,
+                                     f"seed {seed} head {hi_} {head}")
+    assert len(seen) == h.num_patterns
+    # every split chunk of the schedules covers its tile's list exactly once
+    for sched, ptr_name in ((lay.fwd_schedule(), "row_ptr"), (lay.bwd_schedule(), "col_ptr")):
+        cover = {}
+        for head, tile, e0, e1, *_ in sched.tolist():
+            cover.setdefault((head, tile), []).append((e0, e1))
+        for (head, tile), runs in cover.items():
+            ptr = lay.pattern_arrays(int(hp[head]))[ptr_name]
+            runs.sort()
+            assert runs[0][0] == ptr[tile] and runs[-1][1] == ptr[tile + 1]
+            assert all(a[1] == b[0] for a, b in zip(runs, runs[1:]))
+
+
 def test_patterns_are_shared_between_equal_heads():
     heads = [HeadPattern("local", 8), HeadPattern("stride", 8)] * 4 + [HeadPattern("summary", 8, 2, 5)]
     lay = Layout(64, heads, 32, 32)
