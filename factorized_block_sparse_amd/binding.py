@@ -26,6 +26,7 @@ SA_STRIDE_FAR = 7  # blob-only pattern kind: second part of a merged strided hea
 PART_INIT = 1 << 30  # schedule pattern field: first chunk starts from the part state
 SA_BF16, SA_FP32 = 0, 1
 SA_SELF_IF_EMPTY = 1
+SA_NO_SEGMENT_PASS = 2
 SA_BLOB_MAGIC = 0x31415053
 SA_TILE_PARTIAL, SA_TILE_FULL = 0, 1
 SA_XCDS = 8
@@ -37,8 +38,9 @@ EXPORTED = (
 )
 SA_STATIC_SCRATCH_BYTES = 64 << 20  # sparse_attn.h: device array of sparse_attn_bwd_static
 SA_FWD_MAIN, SA_FWD_MERGE, SA_FWD_ALL = 1, 2, 3
-SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_MERGE, SA_BWD_ALL = 1, 2, 4, 7
+SA_BWD_DQ, SA_BWD_DKDV, SA_BWD_MERGE, SA_BWD_SEG, SA_BWD_ALL = 1, 2, 4, 8, 15
 SA_SCHED_FIELDS = 9
+SA_SEGMENT_ROWS = 128
 
 
 class CHeadPattern(ctypes.Structure):
@@ -85,7 +87,10 @@ class CBlobHeader(ctypes.Structure):
                 ("bwdp_sched_len", ctypes.c_int32), ("fwdp_xl_len", ctypes.c_int32),
                 ("bwdp_xl_len", ctypes.c_int32), ("pad0", ctypes.c_int32),
                 ("fwdp_sched_off", ctypes.c_int64), ("bwdp_sched_off", ctypes.c_int64),
-                ("fwdp_xitem_off", ctypes.c_int64), ("bwdp_xitem_off", ctypes.c_int64)]
+                ("fwdp_xitem_off", ctypes.c_int64), ("bwdp_xitem_off", ctypes.c_int64),
+                ("dq_xl_len", ctypes.c_int32), ("seg_xl_len", ctypes.c_int32),
+                ("seg_len", ctypes.c_int32), ("seg_tiles", ctypes.c_int32),
+                ("dq_xitem_off", ctypes.c_int64), ("seg_xitem_off", ctypes.c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -176,16 +181,17 @@ class HeadPattern:
 
 def sparse_attn_layout(n: int, heads, block_q: int = 64, block_k: int = 64,
                        self_if_empty: bool = True, split_keys: int = 0,
-                       split_rows: int = 0) -> np.ndarray:
+                       split_rows: int = 0, segment_pass: bool = True) -> np.ndarray:
     """Build the layout blob (host bytes) for ``heads`` at sequence length ``n``.
 
     ``split_keys`` / ``split_rows`` are the chunk caps of the forward / dQ and
-    dK/dV schedules (0 = the library defaults)."""
+    dK/dV schedules (0 = the library defaults); ``segment_pass=False`` builds
+    it with SA_NO_SEGMENT_PASS."""
     lib = load_library()
     heads = [h if isinstance(h, HeadPattern) else HeadPattern(h.kind, h.l, h.c, h.sub) for h in heads]
     arr = (CHeadPattern * max(1, len(heads)))(*[h.to_c() for h in heads])
-    desc = CLayoutDesc(n, block_q, block_k, len(heads), arr,
-                       SA_SELF_IF_EMPTY if self_if_empty else 0, split_keys, split_rows)
+    flags = (SA_SELF_IF_EMPTY if self_if_empty else 0) | (0 if segment_pass else SA_NO_SEGMENT_PASS)
+    desc = CLayoutDesc(n, block_q, block_k, len(heads), arr, flags, split_keys, split_rows)
     size = ctypes.c_size_t(0)
     _check(lib.sparse_attn_layout(ctypes.byref(desc), None, ctypes.byref(size)), "layout size")
     blob = np.zeros(size.value, dtype=np.uint8)
@@ -198,11 +204,12 @@ class Layout:
     """A built layout: the host blob plus lazily made device copies (one per device)."""
 
     def __init__(self, n: int, heads, block_q: int = 64, block_k: int = 64,
-                 self_if_empty: bool = True, split_keys: int = 0, split_rows: int = 0):
+                 self_if_empty: bool = True, split_keys: int = 0, split_rows: int = 0,
+                 segment_pass: bool = True):
         self.n = int(n)
         self.heads = tuple(heads)
         self.blob = sparse_attn_layout(n, heads, block_q, block_k, self_if_empty, split_keys,
-                                       split_rows)
+                                       split_rows, segment_pass)
         self.header = CBlobHeader.from_buffer_copy(self.blob[: ctypes.sizeof(CBlobHeader)].tobytes())
         self._dev = {}
 
@@ -258,11 +265,13 @@ class Layout:
 
     def xcd_items(self, which: str) -> np.ndarray:
         """[SA_XCDS, len, SA_SCHED_FIELDS] schedule entries in list order ("fwd", "bwd",
-        or "fwdp" / "bwdp" for the second parts of two-part heads)."""
+        "fwdp" / "bwdp" for the second parts of two-part heads, "dq" for the dQ pass,
+        "seg" for the segments of the segment pass)."""
         h = self.header
         off, ln = {"fwd": (h.fwd_xitem_off, h.fwd_xl_len), "bwd": (h.bwd_xitem_off, h.bwd_xl_len),
                    "fwdp": (h.fwdp_xitem_off, h.fwdp_xl_len),
-                   "bwdp": (h.bwdp_xitem_off, h.bwdp_xl_len)}[which]
+                   "bwdp": (h.bwdp_xitem_off, h.bwdp_xl_len),
+                   "dq": (h.dq_xitem_off, h.dq_xl_len), "seg": (h.seg_xitem_off, h.seg_xl_len)}[which]
         return self._arr(off, SA_XCDS * ln * SA_SCHED_FIELDS, np.int32).reshape(SA_XCDS, ln, SA_SCHED_FIELDS)
 
     def part_schedules(self) -> tuple:

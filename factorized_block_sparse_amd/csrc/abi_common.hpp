@@ -19,6 +19,8 @@ struct LaunchInfo {
   bool has_pre;  // some pattern's rows read a key prefix
   int32_t num_merged, fwdp_xl_len, bwdp_xl_len;  // two-part heads and their part lists
   int64_t fwdp_xitem_off, bwdp_xitem_off;
+  int32_t dq_xl_len, seg_xl_len, seg_tiles;  // the dQ pass's list; the segment pass
+  int64_t dq_xitem_off, seg_xitem_off;
 };
 
 inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -64,6 +66,11 @@ inline int validate_common(const void* blob_host, const void* blob_dev, int B, i
   li->bwdp_xl_len = h.bwdp_xl_len;
   li->fwdp_xitem_off = h.fwdp_xitem_off;
   li->bwdp_xitem_off = h.bwdp_xitem_off;
+  li->dq_xl_len = h.dq_xl_len;
+  li->seg_xl_len = h.seg_xl_len;
+  li->seg_tiles = h.seg_tiles;
+  li->dq_xitem_off = h.dq_xitem_off;
+  li->seg_xitem_off = h.seg_xitem_off;
   li->has_pre = false;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

@@ -46,7 +46,8 @@ struct BwdParams {
   const uint8_t* blob;
   const int32_t* qitems;    // per-XCD lists of query-tile entries (the forward's)
   const int32_t* kitems;    // per-XCD lists of key-tile entries
-  int32_t qxl_len, kxl_len;
+  const int32_t* sitems;    // per-XCD lists of segments (segment pass)
+  int32_t qxl_len, kxl_len, sxl_len;
   int32_t B, H, n, num_slots, num_qslots;
   const int32_t* rsched;    // (head, k-tile, first slot, chunks) of each split key tile
   const int32_t* csched;    // (head, q-tile, first slot, chunks) of each split query tile
@@ -614,6 +615,210 @@ void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // --------------------------------------------------------------------------
+// Segment pass: one workgroup per (batch element, segment) of a head whose
+// rows read only keys of their own segment -- a stride head's residue class:
+// tokens r + l t, t < rows, token t reading the tokens t' <= t of its class
+// ("Sparse Transformers 深度解读报告", section 2.2).  The entry gives r, l and
+// rows, so tokens and masks need no map loads.  NT = 32-row sub-tiles of the longest
+// segment; wave w owns sub-tile w, as queries (dQ) and as keys (dK, dV).
+// The segment's Q, K, V and dO rows are staged once, in LDS:
+//   phase 1, wave a, key sub-tiles b <= a: S^T = K_b Q_a^T, dP^T - D and the
+//            dQ products as in the dQ pass; the bf16 P and dS of the pair
+//            (the values the products use) go to LDS;
+//   phase 2, wave b, query sub-tiles a >= b: dV_b^T += dO_a^T P_ab and
+//            dK_b^T += Q_a^T dS_ab, every operand through transposing reads.
+// Each visible pair's S and dP are formed once, every row is read from HBM
+// once and every gradient row written once.  Work per wave: a + 1 pairs in
+// phase 1, NT - b in phase 2.
+// --------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(64 * NT) __attribute__((amdgpu_waves_per_eu(NT <= 3 ? 3 : 2)))
+void bwd_seg_kernel(BwdParams p) {
+  constexpr int NP = NT * (NT + 1) / 2;  // sub-tile pairs b <= a
+  constexpr int KVX = (2 * NT > NP ? 2 * NT : NP) * 32 * kD;
+  // Swizzled [32 * NT][64] tiles; per pair a [32 query rows][64] tile holding
+  // P (columns 0..31, keys of sub-tile b) and dS (columns 32..63).  Phase 2
+  // needs no K or V: the pair tiles take their place once every wave is done
+  // with them (three workgroups per CU for 96-row segments).
+  __shared__ __attribute__((aligned(16))) bf16 qs[NT * 32 * kD], dos[NT * 32 * kD];
+  __shared__ __attribute__((aligned(16))) bf16 kvx[KVX];
+  bf16* const ks = kvx;
+  bf16* const vs = kvx + NT * 32 * kD;
+  bf16* const xs = kvx;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  int b;
+  const int32_t* it8 = xcd_work_entry(p.sitems, p.sxl_len, p.B, &b);
+  if (!it8) return;
+  const int head = it8[0], res = it8[2], rows = it8[3], l = it8[4];
+  const size_t base = (size_t(b) * p.H + head) * size_t(p.n);
+  const int nst = (rows + 31) >> 5;  // sub-tiles of this segment
+  const bool active = w < nst;
+
+  // Staging: wave w fetches rows 32w .. 32w + 31 of the segment (1 KB = 8
+  // rows per direct load); rows past the segment fetch token 0 and are masked.
+  const uint32_t slice_bytes = uint32_t(p.n) * uint32_t(kD * 2);
+  if (active) {
+    const BufRsrc qrs = slice_rsrc(p.q + base * kD, slice_bytes);
+    const BufRsrc krs = slice_rsrc(p.k + base * kD, slice_bytes);
+    const BufRsrc vrs = slice_rsrc(p.v + base * kD, slice_bytes);
+    const BufRsrc drs = slice_rsrc(p.dout + base * kD, slice_bytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 32 * w + 8 * i + (lane >> 3);
+      const uint32_t off = row_chunk_offset(t < rows ? res + l * t : -1, (lane & 7) ^ swz_key(t));
+      const int dst = (32 * w + 8 * i) * kD;
+      dma16_buf(qrs, off, qs + dst);
+      dma16_buf(drs, off, dos + dst);
+      dma16_buf(krs, off, ks + dst);
+      dma16_buf(vrs, off, vs + dst);
+    }
+  }
+  // The lane's query row t = 32 w + l32 of the class (both halves of the
+  // wave hold it); it reads the class's tokens t' <= t.
+  const int r = 32 * w + l32;
+  const bool valid = r < rows;
+  const int tq = valid ? res + l * r : -1;
+  const int hi = valid ? r : -1;
+  // D = dO . O of the lane's row, from its own global reads (the O row is
+  // needed nowhere else), before the staged tiles are waited for.
+  bf16x8 dof[4];
+  float lse2 = 0.f, dsum = 0.f;
+  if (tq >= 0) {
+    const bf16x8* osrc = reinterpret_cast<const bf16x8*>(p.o + (base + tq) * kD);
+    const bf16x8* dsrc = reinterpret_cast<const bf16x8*>(p.dout + (base + tq) * kD);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 oo = osrc[2 * c + g];
+      dof[c] = dsrc[2 * c + g];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum += float(oo[j]) * float(dof[c][j]);
+    }
+    lse2 = p.lse[base + tq] * kLog2e;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dof[c] = bf16x8{};
+  }
+  dsum = pair_sum(dsum);
+  wait_vmem();
+  __syncthreads();
+
+  const float c2 = p.scale_log2;
+  floatx16 dqa[2];
+  dqa[0] = dqa[1] = floatx16{};
+  bf16x8 px[NT][4];  // per key sub-tile: P (keys 0..15, 16..31), dS (likewise), bf16
+  if (active) {
+    bf16x8 qf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(&qs[swz(r, 2 * c + g)]);
+#pragma unroll
+    for (int kb = 0; kb < NT; ++kb) {
+      if (kb > w) break;
+      const bf16* kt = ks + 32 * kb * kD;
+      const bf16* vt = vs + 32 * kb * kD;
+      floatx16 sa = floatx16{}, dp = floatx16{};
+      const int kr = sigma32(l32);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int off = swz(kr, g + 2 * c);
+        sa = mfma_bf16(*reinterpret_cast<const bf16x8*>(&kt[off]), qf[c], sa);
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(&vt[off]), dof[c], dp);
+      }
+      // Register i of half g: class row 32 kb + kappa(i, g).
+      const int hi_rel = hi - (32 * kb + 8 * g);
+      float pr[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cr = 16 * (i >> 3) + (i & 7);
+        const float e = fast_exp2(fmaf(sa[i], c2, -lse2));
+        pr[i] = cr <= hi_rel ? e : 0.f;
+        dsv[i] = pr[i] * (dp[i] - dsum);
+      }
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const bf16x8 db = pack_bf16x8(&dsv[8 * h8]);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+          dqa[fb] = mfma_bf16(load_a_transposed_swz(kt, 16 * h8, 32 * fb, lane), db, dqa[fb]);
+        px[kb][h8] = pack_bf16x8(&pr[8 * h8]);
+        px[kb][2 + h8] = db;
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with K and V
+  if (active) {
+#pragma unroll
+    for (int kb = 0; kb < NT; ++kb) {
+      if (kb > w) break;
+      bf16* x = xs + (w * (w + 1) / 2 + kb) * 32 * kD;
+      // Keys 16 h8 + 8 g .. + 7 of the lane's query row: chunk 2 h8 + g.
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        *reinterpret_cast<bf16x8*>(&x[swz(l32, 2 * h8 + g)]) = px[kb][h8];
+        *reinterpret_cast<bf16x8*>(&x[swz(l32, 4 + 2 * h8 + g)]) = px[kb][2 + h8];
+      }
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  if (tq >= 0) {
+    bf16* row = p.dq + (base + tq) * kD;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = dqa[fb][8 * h8 + j] * p.scale;
+        *reinterpret_cast<bf16x8*>(row + 32 * fb + 16 * h8 + 8 * g) = pack_bf16x8(tmp);
+      }
+  }
+  // Phase 2: key sub-tile w.  Lane l32 holds key 32 w + sigma32(l32) (the
+  // column order of the transposing reads); register i of half g feature
+  // 32 fb + kappa(i, g).
+  floatx16 dka[2], dva[2];
+  dka[0] = dka[1] = dva[0] = dva[1] = floatx16{};
+#pragma unroll
+  for (int a = 0; a < NT; ++a) {
+    if (a < w || a >= nst) continue;
+    const bf16* x = xs + (a * (a + 1) / 2 + w) * 32 * kD;
+    const bf16* qt = qs + 32 * a * kD;
+    const bf16* dt = dos + 32 * a * kD;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 pb = load_a_transposed_swz(x, 16 * h, 0, lane);
+      const bf16x8 sb = load_a_transposed_swz(x, 16 * h, 32, lane);
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        dva[fb] = mfma_bf16(load_a_transposed_swz(dt, 16 * h, 32 * fb, lane), pb, dva[fb]);
+        dka[fb] = mfma_bf16(load_a_transposed_swz(qt, 16 * h, 32 * fb, lane), sb, dka[fb]);
+      }
+    }
+  }
+  const int kr = 32 * w + sigma32(l32);
+  if (kr < rows) {
+    const int tk = res + l * kr;
+    bf16* krow = p.dk + (base + tk) * kD;
+    bf16* vrow = p.dv + (base + tk) * kD;
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        float tk8[8], tv8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          tk8[j] = dka[fb][8 * h8 + j] * p.scale;
+          tv8[j] = dva[fb][8 * h8 + j];
+        }
+        const int f0 = 32 * fb + 16 * h8 + 8 * g;
+        *reinterpret_cast<bf16x8*>(krow + f0) = pack_bf16x8(tk8);
+        *reinterpret_cast<bf16x8*>(vrow + f0) = pack_bf16x8(tv8);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
 // Sum the chunk partials of each split key tile (chunk order) -> dK, dV.
 // --------------------------------------------------------------------------
 // Merge launch: the chunks of each split key tile (dK, dV: 2 * BK * 64
@@ -736,25 +941,30 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return SA_EINVAL;
-  const int64_t gq = int64_t(SA_XCDS) * li.fwd_xl_len * B;
+  const int64_t gq = int64_t(SA_XCDS) * li.dq_xl_len * B;
+  const int64_t gs = int64_t(SA_XCDS) * li.seg_xl_len * B;
   const int64_t gk = int64_t(SA_XCDS) * li.bwd_xl_len * B;
   const int64_t gm = (int64_t(h.red_sched_len) * (2 * bk * kD / 2048) +
                       int64_t(h.comb_sched_len) * (bq * kD / 2048)) * B;
   const int64_t gqp = int64_t(SA_XCDS) * li.fwdp_xl_len * B;
   const int64_t gkp = int64_t(SA_XCDS) * li.bwdp_xl_len * B;
-  if (gq > INT32_MAX || gk > INT32_MAX || gm > INT32_MAX || gqp > INT32_MAX || gkp > INT32_MAX)
+  if (gq > INT32_MAX || gk > INT32_MAX || gm > INT32_MAX || gqp > INT32_MAX || gkp > INT32_MAX ||
+      gs > INT32_MAX)
     return SA_EUNSUPPORTED;
+  if (gs > 0 && (li.seg_tiles < 1 || li.seg_tiles > 4)) return SA_EINVAL;
 
   BwdParams prm;
   prm.blob = static_cast<const uint8_t*>(blob_dev);
-  prm.qitems = reinterpret_cast<const int32_t*>(prm.blob + li.fwd_xitem_off);
+  prm.qitems = reinterpret_cast<const int32_t*>(prm.blob + li.dq_xitem_off);
   prm.kitems = reinterpret_cast<const int32_t*>(prm.blob + li.bwd_xitem_off);
+  prm.sitems = reinterpret_cast<const int32_t*>(prm.blob + li.seg_xitem_off);
+  prm.sxl_len = li.seg_xl_len;
   fill_pattern_table(blob_host, blob_dev, &prm.pats);
   prm.num_qslots = h.num_qslots;
   prm.kgroups = h.red_sched_len;
   prm.rsched = reinterpret_cast<const int32_t*>(prm.blob + h.red_sched_off);
   prm.csched = reinterpret_cast<const int32_t*>(prm.blob + h.comb_sched_off);
-  prm.qxl_len = li.fwd_xl_len;
+  prm.qxl_len = li.dq_xl_len;
   prm.kxl_len = li.bwd_xl_len;
   prm.B = B;
   prm.H = H;
@@ -792,6 +1002,12 @@ extern "C" int sparse_attn_bwd_phases(const void* blob_host, const void* blob_de
     if (li.has_pre) SA_LAUNCH((KN<A, C, true>), g, threads); \
     else SA_LAUNCH((KN<A, C, false>), g, threads);      \
   } while (0)
+  if ((phases & SA_BWD_SEG) && gs > 0) {
+    if (li.seg_tiles == 1) SA_LAUNCH((bwd_seg_kernel<1>), gs, 64);
+    else if (li.seg_tiles == 2) SA_LAUNCH((bwd_seg_kernel<2>), gs, 128);
+    else if (li.seg_tiles == 3) SA_LAUNCH((bwd_seg_kernel<3>), gs, 192);
+    else SA_LAUNCH((bwd_seg_kernel<4>), gs, 256);
+  }
   // Second parts of two-part heads run first in each pass: they leave their
   // sums of every token for the main launch.
   BwdParams pp = prm;

@@ -394,7 +394,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   if (desc->n < 1 || desc->n > kMaxN) return SA_EINVAL;
   if (desc->num_heads < 1 || desc->num_heads > kMaxHeads || !desc->heads) return SA_EINVAL;
   if (!valid_tile(desc->block_q) || !valid_tile(desc->block_k)) return SA_EUNSUPPORTED;
-  if (desc->flags & ~SA_SELF_IF_EMPTY) return SA_EINVAL;
+  if (desc->flags & ~(SA_SELF_IF_EMPTY | SA_NO_SEGMENT_PASS)) return SA_EINVAL;
   if (desc->split_keys < 0 || desc->split_rows < 0) return SA_EINVAL;
   const bool self_if_empty = (desc->flags & SA_SELF_IF_EMPTY) != 0;
   const int32_t n = int32_t(desc->n);
@@ -444,14 +444,32 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   }
   if (pats.size() > 0xffff || num_merged > 0x3ffe) return SA_EUNSUPPORTED;
 
-  std::vector<SchedItem> fwd_items, bwd_items;
-  std::vector<int32_t> red_sched;   // (head, k-tile, first slot, chunks)
-  std::vector<int32_t> comb_sched;  // (head, q-tile, first slot, chunks)
-  int32_t num_slots = 0, num_qslots = 0;
   const int32_t split_rows = desc->split_rows > 0 ? desc->split_rows : SA_SPLIT_ROWS;
   const int32_t split_keys = desc->split_keys > 0 ? desc->split_keys : SA_SPLIT_KEYS;
   const int32_t cap = std::max<int32_t>(1, split_rows / bq);   // q-tiles per dK/dV chunk
   const int32_t qcap = std::max<int32_t>(1, split_keys / bk);  // k-tiles per forward / dQ chunk
+  // Heads whose backward runs in the segment pass: stride heads (each
+  // residue class is a run of layout positions that reads only itself) with
+  // classes of at most SA_SEGMENT_ROWS rows and no split tile.
+  std::vector<uint8_t> seg_head(desc->num_heads, 0);
+  int32_t seg_rows_max = 0;
+  for (int32_t h = 0; h < desc->num_heads && !(desc->flags & SA_NO_SEGMENT_PASS); ++h) {
+    const Pattern& P = pats[head_pat[h]];
+    if (head_part[h] >= 0 || P.p.kind != SA_STRIDE) continue;
+    const int32_t rows = (n + P.p.l - 1) / P.p.l;  // the longest class
+    if (rows > SA_SEGMENT_ROWS) continue;
+    bool split = false;
+    for (int32_t qt = 0; qt < nqt && !split; ++qt) split = P.row_ptr[qt + 1] - P.row_ptr[qt] > qcap;
+    for (int32_t kt = 0; kt < nkt && !split; ++kt) split = P.col_ptr[kt + 1] - P.col_ptr[kt] > cap;
+    if (split) continue;
+    seg_head[h] = 1;
+    seg_rows_max = std::max(seg_rows_max, rows);
+  }
+
+  std::vector<SchedItem> fwd_items, bwd_items, seg_items;
+  std::vector<int32_t> red_sched;   // (head, k-tile, first slot, chunks)
+  std::vector<int32_t> comb_sched;  // (head, q-tile, first slot, chunks)
+  int32_t num_slots = 0, num_qslots = 0;
   int64_t pairs_all = 0, tiles_all = 0;
   for (int32_t h = 0; h < desc->num_heads; ++h) {
     const Pattern& P = pats[head_pat[h]];
@@ -484,6 +502,22 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
         fwd_items.push_back(it);
       }
       num_qslots += chunks;
+    }
+    if (seg_head[h]) {
+      // One item per residue class r: tokens r + l t, t < rows, at layout
+      // positions [off, off + rows) (the maps' class order); work ~ its
+      // visible pairs.
+      const int32_t classes = std::min(P.p.l, n);
+      for (int32_t r = 0, off = 0; r < classes; ++r) {
+        const int32_t rows = (n - r + P.p.l - 1) / P.p.l;
+        SchedItem it{h, off, int32_t(int64_t(rows) * (rows + 1) / 2)};
+        it.e0 = r;
+        it.e1 = rows;
+        it.slot = P.p.l;
+        seg_items.push_back(it);
+        off += rows;
+      }
+      continue;  // no dK/dV items
     }
     for (int32_t kt = 0; kt < nkt; ++kt) {
       if (kt * bk >= n) continue;  // all padding keys
@@ -521,6 +555,7 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   };
   for (auto& it : fwd_items) it.pattern = pattern_field(it.head, head_pat[it.head], it.slot == it.slot0);
   for (auto& it : bwd_items) it.pattern = pattern_field(it.head, head_pat[it.head], it.slot == it.slot0);
+  for (auto& it : seg_items) it.pattern = head_pat[it.head];
   // Second parts: every tile holding a token, none split.
   std::vector<SchedItem> fwdp_items, bwdp_items;
   for (int32_t h = 0; h < desc->num_heads; ++h) {
@@ -557,6 +592,12 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   set_first(fwdp_items, false);
   set_first(bwd_items, true);
   set_first(bwdp_items, true);
+  // The dQ pass: the forward's query-tile entries of the heads without segments.
+  std::vector<SchedItem> dq_items;
+  for (const auto& it : fwd_items)
+    if (!seg_head[it.head]) dq_items.push_back(it);
+  const std::vector<int32_t> dq_sched = sorted_schedule(dq_items);
+  const std::vector<int32_t> seg_sched = sorted_schedule(seg_items);
   const std::vector<int32_t> fwd_sched = sorted_schedule(fwd_items);
   const std::vector<int32_t> bwd_sched = sorted_schedule(bwd_items);
   const std::vector<int32_t> fwdp_sched = sorted_schedule(fwdp_items);
@@ -566,6 +607,9 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   const int32_t bwd_xl_len = xcd_lists(bwd_items, bwd_xl);
   const int32_t fwdp_xl_len = fwdp_items.empty() ? 0 : xcd_lists(fwdp_items, fwdp_xl);
   const int32_t bwdp_xl_len = bwdp_items.empty() ? 0 : xcd_lists(bwdp_items, bwdp_xl);
+  std::vector<int32_t> dq_xl, seg_xl;
+  const int32_t dq_xl_len = xcd_lists(dq_items, dq_xl);
+  const int32_t seg_xl_len = seg_items.empty() ? 0 : xcd_lists(seg_items, seg_xl);
   // The entries in list order (padding: all -1).
   auto list_items = [](const std::vector<int32_t>& xl, const std::vector<int32_t>& sched) {
     std::vector<int32_t> out;
@@ -579,6 +623,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
   const std::vector<int32_t> bwd_xitem = list_items(bwd_xl, bwd_sched);
   const std::vector<int32_t> fwdp_xitem = list_items(fwdp_xl, fwdp_sched);
   const std::vector<int32_t> bwdp_xitem = list_items(bwdp_xl, bwdp_sched);
+  const std::vector<int32_t> dq_xitem = list_items(dq_xl, dq_sched);
+  const std::vector<int32_t> seg_xitem = list_items(seg_xl, seg_sched);
 
   // Two passes: size, then write.
   for (int pass = 0; pass < 2; ++pass) {
@@ -603,6 +649,8 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwdp_sched_off = w.put(bwdp_sched);
     hdr.fwdp_xitem_off = w.put(fwdp_xitem);
     hdr.bwdp_xitem_off = w.put(bwdp_xitem);
+    hdr.dq_xitem_off = w.put(dq_xitem);
+    hdr.seg_xitem_off = w.put(seg_xitem);
     for (size_t i = 0; i < pats.size(); ++i) {
       const Pattern& P = pats[i];
       sa_pattern_rec& r = recs[i];
@@ -669,6 +717,10 @@ int build(const sa_layout_desc* desc, uint8_t* blob, size_t* blob_bytes) {
     hdr.bwdp_sched_len = int32_t(bwdp_items.size());
     hdr.fwdp_xl_len = fwdp_xl_len;
     hdr.bwdp_xl_len = bwdp_xl_len;
+    hdr.dq_xl_len = dq_xl_len;
+    hdr.seg_xl_len = seg_xl_len;
+    hdr.seg_len = int32_t(seg_items.size());
+    hdr.seg_tiles = (seg_rows_max + 31) / 32;
     std::memcpy(blob + hdr_at, &hdr, sizeof(hdr));
     std::memcpy(blob + rec_at, recs.data(), recs.size() * sizeof(sa_pattern_rec));
     *blob_bytes = size_t(total);
@@ -726,7 +778,11 @@ extern "C" int sparse_attn_layout_check(const void* blob_host, size_t blob_bytes
       !in_blob(h.fwdp_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.fwdp_sched_len), total) ||
       !in_blob(h.bwdp_sched_off, 4 * SA_SCHED_FIELDS * int64_t(h.bwdp_sched_len), total) ||
       !in_blob(h.fwdp_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.fwdp_xl_len, total) ||
-      !in_blob(h.bwdp_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwdp_xl_len, total))
+      !in_blob(h.bwdp_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.bwdp_xl_len, total) ||
+      h.dq_xl_len < 0 || h.seg_xl_len < 0 || h.seg_len < 0 || h.seg_tiles < 0 ||
+      h.seg_tiles > (SA_SEGMENT_ROWS + 31) / 32 || (h.seg_tiles == 0) != (h.seg_len == 0) ||
+      !in_blob(h.dq_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.dq_xl_len, total) ||
+      !in_blob(h.seg_xitem_off, 4 * SA_SCHED_FIELDS * int64_t(SA_XCDS) * h.seg_xl_len, total))
     return SA_EINVAL;
   for (int32_t i = 0; i < h.num_patterns; ++i) {
     sa_pattern_rec r;

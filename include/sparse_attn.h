@@ -93,6 +93,9 @@ enum sa_dtype { SA_BF16 = 0, SA_FP32 = 1 };
 /* Layout flag: a row whose set is empty reads itself (report section 2.2 gives
  * no rule; the blog post's section 02 forbids empty rows). */
 #define SA_SELF_IF_EMPTY 1u
+/* Layout flag: no segment pass (see sa_blob_header); every head's backward
+ * then runs through the dQ and dK/dV passes, for comparisons. */
+#define SA_NO_SEGMENT_PASS 2u
 
 /* One head's pattern.  c is the summary width (SA_SUMMARY, SA_FIXED_MERGED)
  * or the number of leading global tokens (SA_LOCAL_GLOBAL); sub is used by
@@ -110,7 +113,7 @@ typedef struct {
   int32_t block_k;               /* key-tile columns: 32, 64 or 128 */
   int32_t num_heads;             /* 1 .. 4096 */
   const sa_head_pattern* heads;  /* num_heads entries, host memory */
-  uint32_t flags;                /* SA_SELF_IF_EMPTY or 0 */
+  uint32_t flags;                /* SA_SELF_IF_EMPTY, SA_NO_SEGMENT_PASS, or 0 */
   int32_t split_keys;            /* query-tile chunk cap in keys; 0 = SA_SPLIT_KEYS */
   int32_t split_rows;            /* key-tile chunk cap in query rows; 0 = SA_SPLIT_ROWS */
 } sa_layout_desc;
@@ -150,7 +153,7 @@ typedef struct {
  * ------------------------------------------------------------------------- */
 
 #define SA_BLOB_MAGIC 0x31415053u /* "SPA1" */
-#define SA_BLOB_VERSION 10u
+#define SA_BLOB_VERSION 11u
 #define SA_SCHED_FIELDS 9
 /* Default chunk caps (sa_layout_desc.split_rows / split_keys).  Key tiles read
  * by more than split_rows query rows are split into chunks of at most that
@@ -161,6 +164,8 @@ typedef struct {
  * order.  A cap of at least n disables splitting. */
 #define SA_SPLIT_ROWS 1536
 #define SA_SPLIT_KEYS 3072
+/* Longest segment of the segment pass, in rows. */
+#define SA_SEGMENT_ROWS 128
 /* Number of accelerator complex dies (XCDs, each with its own L2) that
  * workgroups are dealt to round-robin on MI355X. */
 #define SA_XCDS 8
@@ -248,6 +253,25 @@ typedef struct {
   int64_t bwdp_sched_off;   /* the same over second-part k-tiles */
   int64_t fwdp_xitem_off;   /* int32[SA_XCDS * fwdp_xl_len * SA_SCHED_FIELDS], as fwd_xitem */
   int64_t bwdp_xitem_off;   /* int32[SA_XCDS * bwdp_xl_len * SA_SCHED_FIELDS] */
+  /* Segment pass of the backward.  A head whose rows read keys of their own
+   * segment only -- a contiguous run of layout positions closed under the
+   * pattern: an SA_STRIDE head's residue classes ("Sparse Transformers
+   * 深度解读报告", section 2.2) -- takes dQ, dK and dV from one workgroup
+   * per segment instead of the dQ and dK/dV passes, when its segments hold
+   * at most SA_SEGMENT_ROWS rows, none of its tiles is split and the layout
+   * was built without SA_NO_SEGMENT_PASS.  Its tiles then leave the dQ list
+   * and the backward schedule; the forward is unchanged. */
+  int32_t dq_xl_len, seg_xl_len;
+  int32_t seg_len;          /* segments of one batch element */
+  int32_t seg_tiles;        /* 32-row sub-tiles of the longest segment (1..4); 0 if none */
+  int64_t dq_xitem_off;     /* int32[SA_XCDS * dq_xl_len * SA_SCHED_FIELDS]: the forward's
+                               query-tile entries of the heads without segments, per-XCD
+                               lists as fwd_xitem (the dQ pass's work) */
+  int64_t seg_xitem_off;    /* int32[SA_XCDS * seg_xl_len * SA_SCHED_FIELDS]: (head, first
+                               position, residue r, rows, stride l, pattern field, -1, 1,
+                               -1) of each segment -- the class of tokens r + l t,
+                               t < rows, in which token t reads t' <= t -- per-XCD lists
+                               as fwd_xitem */
 } sa_blob_header;
 
 /* Build the layout.  With blob == NULL, only *blob_bytes is set (size query).
@@ -313,20 +337,23 @@ int sparse_attn_bwd(const void* blob_host, const void* blob_dev, int B, int H, i
                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
                     void* workspace, size_t ws_bytes, float scale, void* stream);
 
-/* The backward's three launches, separately, for callers that interleave
- * other work between them or time them one by one:
- *   SA_BWD_DQ     per query tile (long tiles in chunks): D_i = dO_i . O_i
- *                 (kept in the workspace) and dQ, or float32 partial dQ of
- *                 split tiles (workspace); second parts of two-part heads
- *                 first, in a launch of their own;
- *   SA_BWD_DKDV   per key tile (long tiles in chunks): dK and dV, or float32
- *                 partial sums of split tiles (workspace); second parts
- *                 first, likewise;
+/* The backward's launches, separately, for callers that interleave other
+ * work between them or time them one by one:
+ *   SA_BWD_SEG    per segment of the heads the segment pass runs (see
+ *                 sa_blob_header): their dQ, dK and dV, independent of the
+ *                 other phases;
+ *   SA_BWD_DQ     per query tile of the other heads (long tiles in chunks):
+ *                 D_i = dO_i . O_i (kept in the workspace) and dQ, or
+ *                 float32 partial dQ of split tiles (workspace); second parts
+ *                 of two-part heads first, in a launch of their own;
+ *   SA_BWD_DKDV   per key tile of the other heads (long tiles in chunks): dK
+ *                 and dV, or float32 partial sums of split tiles (workspace);
+ *                 second parts first, likewise;
  *   SA_BWD_MERGE  sums the partials of split query and key tiles in a fixed
  *                 order and writes their dQ, dK, dV.
  * Phases must run in this order on one stream with the same arguments and
  * workspace; sparse_attn_bwd is sparse_attn_bwd_phases(..., SA_BWD_ALL). */
-enum { SA_BWD_DQ = 1, SA_BWD_DKDV = 2, SA_BWD_MERGE = 4, SA_BWD_ALL = 7 };
+enum { SA_BWD_DQ = 1, SA_BWD_DKDV = 2, SA_BWD_MERGE = 4, SA_BWD_SEG = 8, SA_BWD_ALL = 15 };
 int sparse_attn_bwd_phases(const void* blob_host, const void* blob_dev, int B, int H, int d,
                            int dtype, const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dO, void* dq, void* dk, void* dv,

@@ -125,6 +125,20 @@ def test_small_cases_every_element(case):
     _check_dense(lay, heads, B, n, inp)
 
 
+STRIDE_CASES = [c for c in SMALL if any(h.kind == "stride" for h in c[5])]
+
+
+@pytest.mark.parametrize("case", STRIDE_CASES, ids=[c[0] for c in STRIDE_CASES])
+def test_stride_heads_through_the_tile_passes(case):
+    """The same cases with the segment pass off (SA_NO_SEGMENT_PASS): stride heads run
+    through the dQ and dK/dV passes; the default layouts above run them in segments."""
+    name, B, n, bq, bk, heads = case[:6]
+    lay = Layout(n, heads, bq, bk, split_keys=case[6] if len(case) > 6 else 0, segment_pass=False)
+    assert lay.header.seg_len == 0
+    inp = W.make_inputs(B, len(heads), n, 64, seed=zlib.crc32(name.encode()) % 10000)
+    _check_dense(lay, heads, B, n, inp)
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9100 + seed)
     n = int(rng.integers(1, 1501))

@@ -342,6 +342,11 @@ def test_xcd_lists_cover_every_schedule_entry_once(n, bq, bk, heads):
                 prev_max = rs[-1]
 
 
+def _segment_heads(lay) -> set:
+    items = lay.xcd_items("seg").reshape(-1, bd.SA_SCHED_FIELDS)
+    return {int(r[0]) for r in items if r[0] >= 0}
+
+
 @pytest.mark.parametrize("n,bq,bk,heads", [
     (12288, 64, 64, [HeadPattern("sameblock", 128), HeadPattern("summary", 128, 32, 0),
                      HeadPattern("summary", 128, 32, 3)]),
@@ -358,8 +363,12 @@ def test_dkdv_chunks_partition_every_csc_column(n, bq, bk, heads):
     slots = sorted(int(r[4]) for r in bs if r[4] >= 0)
     assert slots == list(range(h.num_slots))
     red = {(int(r[0]), int(r[1])): (int(r[2]), int(r[3])) for r in rs}
+    seg = _segment_heads(lay)
     for head in range(len(heads)):
         a = lay.pattern_arrays(int(lay.head_pattern_index()[head]))
+        if head in seg:  # the segment pass runs this head's backward
+            assert not any(r[0] == head for r in bs)
+            continue
         for kt in range(h.nkt):
             if kt * bk >= n:
                 continue
@@ -445,6 +454,71 @@ def test_chunk_caps_are_layout_parameters(split_keys, split_rows):
     for i in range(ref.num_patterns):  # the caps change schedules only
         for key, arr in ref.pattern_arrays(i).items():
             np.testing.assert_array_equal(lay.pattern_arrays(i)[key], arr)
+
+
+@pytest.mark.parametrize("n,bq,bk,heads", [
+    (12288, 32, 32, [HeadPattern("local", 128), HeadPattern("stride", 128)] * 2),
+    (3072, 64, 64, [HeadPattern("local", 64), HeadPattern("stride", 64)]),
+    (1000, 64, 32, [HeadPattern("stride", 7), HeadPattern("stride", 9), HeadPattern("summary", 8, 2, 1)]),
+    (100, 32, 32, [HeadPattern("stride", 1000), HeadPattern("stride", 1)]),
+    (4097, 128, 128, [HeadPattern("stride", 32), HeadPattern("stride", 31), HeadPattern("strided_merged", 64)]),
+])
+def test_segments_are_the_stride_classes(n, bq, bk, heads):
+    """Segment pass: each qualifying stride head is listed as its residue classes -- runs of
+    layout positions whose rows read only keys of the same run and whose keys only rows
+    of it read (checked against the oracle's sets), each at most SA_SEGMENT_ROWS rows --
+    and leaves the dQ list and the backward schedule; every other head keeps its items."""
+    lay = Layout(n, heads, bq, bk)
+    h = lay.header
+    items = lay.xcd_items("seg").reshape(-1, bd.SA_SCHED_FIELDS)
+    items = items[items[:, 0] >= 0]
+    hp = lay.head_pattern_index()
+    expect = {hh for hh, x in enumerate(heads) if x.kind == "stride" and -(-n // x.l) <= bd.SA_SEGMENT_ROWS}
+    assert _segment_heads(lay) == expect
+    assert h.seg_len == len(items)
+    longest = 0
+    for hh in sorted(expect):
+        l = heads[hh].l
+        mine = sorted((int(r[1]), int(r[3])) for r in items if r[0] == hh)
+        assert all(tuple(r[[4, 6, 7, 8]]) == (l, -1, 1, -1) and r[5] == hp[hh]
+                   for r in items if r[0] == hh)
+        assert sorted(int(r[2]) for r in items if r[0] == hh) == list(range(min(l, n)))
+        qmap = lay.pattern_arrays(int(hp[hh]))["qmap"]
+        pos = 0
+        res = {int(r[1]): int(r[2]) for r in items if r[0] == hh}
+        for r, (start, rows) in enumerate(mine):
+            assert res[start] == r
+            assert start == pos and rows == len(range(r, n, l)) and 1 <= rows <= bd.SA_SEGMENT_ROWS
+            toks = qmap[start:start + rows]
+            np.testing.assert_array_equal(toks, np.arange(r, n, l))
+            ts = set(toks.tolist())
+            for i in toks[:: max(1, rows // 7)]:
+                assert set(M.row_keys(M.STRIDE, int(i), n, l).tolist()) <= ts
+                assert set(M.rows_seeing(M.STRIDE, int(i), n, l).tolist()) <= ts
+            pos += rows
+            longest = max(longest, rows)
+        assert pos == n and len(mine) == min(l, n)
+    assert h.seg_tiles == -(-longest // 32)
+    fwd = lay.xcd_items("fwd").reshape(-1, bd.SA_SCHED_FIELDS)
+    dq = lay.xcd_items("dq").reshape(-1, bd.SA_SCHED_FIELDS)
+    want = sorted(tuple(r) for r in fwd.tolist() if r[0] >= 0 and r[0] not in expect)
+    assert sorted(tuple(r) for r in dq.tolist() if r[0] >= 0) == want
+    bs = lay.bwd_schedule()
+    assert {int(r[0]) for r in bs} == set(range(len(heads))) - expect
+    # Without the pass: no segments, the dQ list is the forward's, every head in the schedule.
+    off = Layout(n, heads, bq, bk, segment_pass=False)
+    assert off.header.seg_len == off.header.seg_tiles == off.header.seg_xl_len == 0
+    f2, d2 = (off.xcd_items(x).reshape(-1, bd.SA_SCHED_FIELDS) for x in ("fwd", "dq"))
+    assert sorted(map(tuple, f2.tolist())) == sorted(map(tuple, d2.tolist()))
+    assert {int(r[0]) for r in off.bwd_schedule()} == set(range(len(heads)))
+
+
+def test_segment_pass_skips_heads_with_split_tiles():
+    """A stride head whose tiles are split (caps below its lists) keeps the tile passes."""
+    heads = [HeadPattern("stride", 8), HeadPattern("local", 8)]
+    assert _segment_heads(Layout(1000, heads, 32, 32)) == {0}
+    assert _segment_heads(Layout(1000, heads, 32, 32, split_keys=32)) == set()
+    assert _segment_heads(Layout(1000, heads, 32, 32, split_rows=32)) == set()
 
 
 def test_padding_overhead_closed_form_12288():
@@ -635,7 +709,7 @@ def test_fwd_bwd_argument_errors_before_any_launch():
     assert g(B=0) == bd.SA_OK
     gp = lambda ph: lib.sparse_attn_bwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake, fake,
                                                fake, fake, fake, fake, 1 << 30, 0.0, ph, None)
-    assert gp(0) == bd.SA_EINVAL and gp(8) == bd.SA_EINVAL
+    assert gp(0) == bd.SA_EINVAL and gp(16) == bd.SA_EINVAL
     fp = lambda ph: lib.sparse_attn_fwd_phases(hb, fake, 1, 2, 64, 0, fake, fake, fake, fake, fake,
                                                fake, 1 << 30, 0.0, ph, None)
     assert fp(0) == bd.SA_EINVAL and fp(4) == bd.SA_EINVAL
