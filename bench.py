@@ -66,6 +66,9 @@ def kernel_work(label: str, B: int, H: int, n: int, pairs: int):
         return 2 * D * pairs, rows * (6 * D * 2 + 4 + 4)         # Q,K,V,O,dO read, dQ write; LSE, D
     if label == "bwd_dkdv":
         return 6 * D * pairs, rows * (6 * D * 2 + 8)             # Q,K,V,dO read, dK,dV write; LSE, D
+    # Segment pass (stride heads' classes): all 8 d per pair in one kernel.
+    if label == "bwd_seg":
+        return 8 * D * pairs, rows * (8 * D * 2 + 4)             # Q,K,V,O,dO read, dQ,dK,dV write; LSE
     if label in ("fwd_merge", "bwd_merge"):
         return 0, 0  # merges of split tiles: no useful FLOPs of their own
     raise ValueError(label)
@@ -83,7 +86,27 @@ def algorithmic_bytes(w) -> int:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "n12288_fixed_strided_hbm_traffic.txt")
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel", "fwd_merge": "fwd_merge_kernel", "bwd_dq": "bwd_dq_kernel",
-                "bwd_dkdv": "bwd_dkdv_kernel", "bwd_merge": "bwd_merge_kernel"}
+                "bwd_dkdv": "bwd_dkdv_kernel", "bwd_merge": "bwd_merge_kernel", "bwd_seg": "bwd_seg_kernel"}
+
+
+def segment_heads(lay) -> tuple:
+    """(heads run by the segment pass, their visible pairs) for one batch element."""
+    items = lay.xcd_items("seg").reshape(-1, 9)
+    heads = sorted({int(r[0]) for r in items if r[0] >= 0})
+    hp = lay.head_pattern_index()
+    return len(heads), sum(int(lay.pattern_rec(int(hp[h])).pairs) for h in heads)
+
+
+def launch_work(label: str, w, lay) -> tuple:
+    """kernel_work over the heads a launch processes: the segment pass takes the
+    segmented heads, the dQ and dK/dV passes the others."""
+    hs, ps = segment_heads(lay)
+    pairs = lay.pairs_per_batch()
+    if label == "bwd_seg":
+        return kernel_work(label, w.B, hs, w.n, ps * w.B)
+    if label in ("bwd_dq", "bwd_dkdv"):
+        return kernel_work(label, w.B, w.H - hs, w.n, (pairs - ps) * w.B)
+    return kernel_work(label, w.B, w.H, w.n, pairs * w.B)
 
 
 def kernel_sources_hash() -> str:
@@ -629,9 +652,11 @@ def main():
             calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, fws=fws, ph=ph:
                           bd.sparse_attn_fwd(lay, q, k, v, out=o, lse=lse, workspace=fws, phases=ph)))
         if w.backward:
-            for label, ph in (("bwd_dq", bd.SA_BWD_DQ), ("bwd_dkdv", bd.SA_BWD_DKDV),
-                              ("bwd_merge", bd.SA_BWD_MERGE)):
+            for label, ph in (("bwd_seg", bd.SA_BWD_SEG), ("bwd_dq", bd.SA_BWD_DQ),
+                              ("bwd_dkdv", bd.SA_BWD_DKDV), ("bwd_merge", bd.SA_BWD_MERGE)):
                 if label == "bwd_merge" and not (split_q or split_k):
+                    continue
+                if label == "bwd_seg" and lay.header.seg_len == 0:
                     continue
                 calls.append((label, lambda lay=lay, q=q, k=k, v=v, o=o, lse=lse, do=do, ws=ws, grads=grads, ph=ph:
                               bd.sparse_attn_bwd(lay, q, k, v, o, lse, do, workspace=ws, grads=grads, phases=ph)))
@@ -727,7 +752,7 @@ def main():
         for label, _ in r["calls"]:
             t = per_call_ms[idx]
             ms += t
-            fl, by = kernel_work(label, w.B, w.H, w.n, r["pairs"])
+            fl, by = launch_work(label, w, r["lay"])
             kernels.append(dict(workload=w.name, kernel=label, ms=t, flops=fl, bytes=by))
             idx += 1
         tf = r["useful"] / (ms * 1e-3) / 1e12

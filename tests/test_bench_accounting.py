@@ -111,3 +111,25 @@ def test_cpu_baseline_task_runs_what_it_counts(monkeypatch):
     done, fl = bench._cpu_task((("t", 0, 0), rows, time.time() + 60))
     assert sorted(calls) == ["bwd", "fwd"] and done == 3
     assert fl == 12 * 64 * sum(OM.row_keys(OM.LOCAL, i, n, 5).size for i in rows)
+
+
+def test_segment_pass_takes_its_heads_out_of_the_tile_passes():
+    """Strided n = 12,288: the segment pass carries the eight stride heads (8 d per
+    pair), the dQ and dK/dV passes the eight local heads; the useful FLOPs still add
+    up to 12 d per visible pair."""
+    from factorized_block_sparse_amd import binding as bd
+    w = W.WORKLOADS["strided_n12288"]
+    lay = bd.Layout(w.n, w.heads, w.block_q, w.block_k)
+    hs, ps = bench.segment_heads(lay)
+    assert hs == 8 and lay.header.seg_len == 8 * 128 and lay.header.seg_tiles == 3
+    stride_pairs = sum(OM.row_keys(OM.STRIDE, i, w.n, 128).size for i in range(w.n))
+    assert ps == 8 * stride_pairs
+    total = sum(bench.launch_work(k, w, lay)[0] for k in ("fwd", "bwd_seg", "bwd_dq", "bwd_dkdv"))
+    assert total == 12 * 64 * lay.pairs_per_batch() * w.B
+    rows = w.B * 8 * w.n
+    assert bench.launch_work("bwd_seg", w, lay)[1] == rows * (8 * 64 * 2 + 4)
+    assert bench.launch_work("bwd_dq", w, lay)[1] == rows * (6 * 64 * 2 + 8)
+    off = bd.Layout(w.n, w.heads, w.block_q, w.block_k, segment_pass=False)
+    assert bench.segment_heads(off) == (0, 0)
+    assert bench.launch_work("bwd_dq", w, off) == bench.kernel_work("bwd_dq", w.B, w.H, w.n,
+                                                                   off.pairs_per_batch() * w.B)
