@@ -72,6 +72,11 @@ SMALL = [
     ("strided_merged_q128_k64", 1, 640, 128, 64, [HeadPattern("strided_merged", 40)]),
     ("split_strided_merged", 1, 2300, 64, 64, [HeadPattern("strided_merged", 1100),
                                                HeadPattern("strided_merged", 16)], 512),
+    # stride heads in the segment pass: classes of 125 / 112 rows (four sub-tiles), 78 and
+    # 59 rows (three and two), ragged last sub-tiles
+    ("stride_segments_4", 2, 1000, 64, 64, [HeadPattern("stride", 8), HeadPattern("local", 8),
+                                            HeadPattern("stride", 9)]),
+    ("stride_segments_3", 1, 700, 32, 32, [HeadPattern("stride", 9), HeadPattern("stride", 12)]),
     # 128-row query tiles over 32-key tiles (one-wave dK/dV workgroups in two 64-row steps)
     ("tiles128x32", 1, 400, 128, 32, [HeadPattern("local", 40), HeadPattern("stride", 40),
                                       HeadPattern("sameblock", 50), HeadPattern("summary", 64, 8, 1),
