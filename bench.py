@@ -820,7 +820,7 @@ def main():
                    "per_workload": per_wl, "kernels": kernels},
         "calibration": calibration,
         "preroll": preroll,
-        "scaling": scaling,
+        "length_scaling": scaling,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_sources_sha256": kernel_sources_hash(),

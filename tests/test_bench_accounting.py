@@ -133,3 +133,22 @@ def test_segment_pass_takes_its_heads_out_of_the_tile_passes():
     assert bench.segment_heads(off) == (0, 0)
     assert bench.launch_work("bwd_dq", w, off) == bench.kernel_work("bwd_dq", w.B, w.H, w.n,
                                                                    off.pairs_per_batch() * w.B)
+
+
+def test_bench_line_has_no_duplicate_keys():
+    """The JSON line is one dict literal: a repeated key would silently replace a
+    contract field (e.g. "scaling": "weak")."""
+    import ast
+    import os
+    src = open(os.path.join(os.path.dirname(bench.__file__), "bench.py")).read()
+    found = 0
+    for node in ast.walk(ast.parse(src)):
+        if isinstance(node, ast.Assign) and any(getattr(t, "id", None) == "line" for t in node.targets) \
+                and isinstance(node.value, ast.Dict):
+            keys = [k.value for k in node.value.keys if isinstance(k, ast.Constant)]
+            assert len(keys) == len(set(keys)), sorted(k for k in keys if keys.count(k) > 1)
+            assert {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                    "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                    "roofline", "cpu_baseline"} <= set(keys)
+            found += 1
+    assert found == 1
