@@ -619,12 +619,13 @@ void bwd_dkdv_kernel(BwdParams p) {
 // rows read only keys of their own segment -- a stride head's residue class:
 // tokens r + l t, t < rows, token t reading the tokens t' <= t of its class
 // ("Sparse Transformers 深度解读报告", section 2.2).  The entry gives r, l and
-// rows, so tokens and masks need no map loads.  NT = 32-row sub-tiles of the longest
-// segment; wave w owns sub-tile w, as queries (dQ) and as keys (dK, dV).
-// The segment's Q, K, V and dO rows are staged once, in LDS:
+// rows, so tokens and masks need no map loads.  NT = 32-row sub-tiles of the
+// longest segment; wave w owns sub-tile w, as queries (dQ) and as keys (dK,
+// dV).  The segment's Q, K, V and dO rows are staged once, in LDS:
 //   phase 1, wave a, key sub-tiles b <= a: S^T = K_b Q_a^T, dP^T - D and the
-//            dQ products as in the dQ pass; the bf16 P and dS of the pair
-//            (the values the products use) go to LDS;
+//            dQ products as in the dQ pass; the bf16 P and dS of each pair
+//            (the values the products use) stay in registers and go to LDS,
+//            into the space of K and V, once every wave is done with those;
 //   phase 2, wave b, query sub-tiles a >= b: dV_b^T += dO_a^T P_ab and
 //            dK_b^T += Q_a^T dS_ab, every operand through transposing reads.
 // Each visible pair's S and dP are formed once, every row is read from HBM
