@@ -602,6 +602,33 @@ def test_layout_buffer_too_small_and_check():
     assert lib.sparse_attn_layout_check(None, need) == bd.SA_EINVAL
 
 
+def test_layout_check_rejects_bad_segment_fields():
+    """The segment pass's header fields are checked like the others: sub-tile count in
+    1..4 exactly when there are segments, lists inside the blob."""
+    lib = bd.load_library()
+    lay = Layout(1000, [HeadPattern("stride", 8), HeadPattern("local", 8)], 64, 64)
+    h = lay.header
+    assert h.seg_len == 8 and h.seg_tiles == 4
+    assert lib.sparse_attn_layout_check(lay.blob.ctypes.data, lay.blob.size) == 0
+
+    def patched(**fields):
+        hdr = bd.CBlobHeader.from_buffer_copy(lay.blob[: ctypes.sizeof(bd.CBlobHeader)].tobytes())
+        for k, v in fields.items():
+            setattr(hdr, k, v)
+        blob = lay.blob.copy()
+        blob[: ctypes.sizeof(hdr)] = np.frombuffer(bytes(hdr), dtype=np.uint8)
+        return lib.sparse_attn_layout_check(blob.ctypes.data, blob.size)
+
+    assert patched() == 0
+    assert patched(seg_tiles=5) == bd.SA_EINVAL
+    assert patched(seg_tiles=0) == bd.SA_EINVAL
+    assert patched(seg_len=-1) == bd.SA_EINVAL
+    assert patched(seg_xitem_off=int(lay.blob.size)) == bd.SA_EINVAL
+    assert patched(dq_xl_len=1 << 20) == bd.SA_EINVAL
+    off = Layout(1000, [HeadPattern("stride", 8)], 64, 64, segment_pass=False)
+    assert off.header.seg_len == 0 and off.header.seg_tiles == 0
+
+
 def test_library_exports_every_declared_symbol():
     lib = bd.load_library()
     with open(os.path.join(ROOT, "include", "sparse_attn.h")) as f:
