@@ -44,12 +44,32 @@ SOURCES = ("factorized_block_sparse_amd/csrc/device_common.hpp",
 COPY_KERNEL_MARK = "copyBuffer"  # the runtime's device-to-device copy kernel
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without comments and with runs of whitespace collapsed: what
+    the compiler sees of it (the sources hold no comment markers inside string
+    literals)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
-    """sha256 over the kernel and layout sources (the code the counters describe)."""
+    """sha256 over the code of the kernel and layout sources (the code the
+    counters describe; comments and layout of the text do not count)."""
     h = hashlib.sha256()
     for rel in SOURCES:
-        with open(os.path.join(_ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+        with open(os.path.join(_ROOT, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + code_text(f.read()).encode() + b"\0")
     return h.hexdigest()
 
 

@@ -35,7 +35,8 @@
  *     pattern of head h; H must equal the layout's num_heads.
  *   - d must be 64.  dtype SA_BF16 (bfloat16 data, float32 accumulation)
  *     for forward and backward, with n < 2^25 (SA_EUNSUPPORTED otherwise);
- *     SA_FP32 (float32 throughout) for forward.
+ *     SA_FP32 (float32 throughout) for forward, on layouts without two-part
+ *     heads (SA_STRIDED_MERGED; SA_EUNSUPPORTED otherwise).
  *   - Tile shapes run by the kernels: bf16, any block_q of 32, 64, 128 with
  *     block_k of 32 or 64, and block_q = block_k = 128; fp32, block_k = 32.
  *     Other layouts build, and their calls return SA_EUNSUPPORTED.

@@ -159,20 +159,36 @@ def _random_case(seed):
             heads.append(HeadPattern(kind, l, int(rng.integers(0, 40))))
         else:
             heads.append(HeadPattern(kind, l))
-    return (int(rng.integers(1, 3)), n, bq, bk, heads, int(rng.integers(32, 512)),
-            int(rng.integers(32, 512)))
+    caps = (int(rng.integers(32, 512)), int(rng.integers(32, 512)))
+    if (seed // 7) % 2 == 1:
+        caps = (0, 0)  # the default caps: few splits, stride heads in the segment pass
+    return (int(rng.integers(1, 3)), n, bq, bk, heads) + caps
 
 
-@pytest.mark.parametrize("seed", range(14))
+@pytest.mark.parametrize("seed", range(28))
 def test_random_small_layouts_every_element(seed):
     """Seeded random layouts (n up to 1,500, one to four heads of any kind with random
-    l, c and sub-block, every tile shape, random chunk caps so that tiles split):
-    every element of O, LSE, dQ, dK, dV against the oracle."""
+    l, c and sub-block, every tile shape; random chunk caps so that tiles split, or the
+    default caps): every element of O, LSE, dQ, dK, dV against the oracle."""
     B, n, bq, bk, heads, sk, sr = _random_case(seed)
     print(f"seed {seed}: B={B} n={n} tiles={bq}x{bk} caps={sk},{sr} heads={heads}", flush=True)
     lay = Layout(n, heads, bq, bk, split_keys=sk, split_rows=sr)
     inp = W.make_inputs(B, len(heads), n, 64, seed=9200 + seed)
     _check_dense(lay, heads, B, n, inp)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp32_forward_random_layouts(seed):
+    """float32 forward on seeded random layouts (query tiles 32, 64, 128 over 32-key
+    tiles; random caps): every element of O and LSE."""
+    B, n, _, _, heads, sk, _ = _random_case(100 + seed)
+    # two-part heads run in bf16 only (SA_EUNSUPPORTED for float32): their stride part instead
+    heads = [HeadPattern("stride", h.l) if h.kind == "strided_merged" else h for h in heads]
+    bq = (32, 64, 128)[seed % 3]
+    print(f"fp32 seed {seed}: B={B} n={n} tiles={bq}x32 cap={sk} heads={heads}", flush=True)
+    lay = Layout(n, heads, bq, 32, split_keys=sk)
+    inp = W.make_inputs(B, len(heads), n, 64, seed=9300 + seed, dtype="fp32")
+    _check_dense(lay, heads, B, n, inp, backward=False, fp32=True)
 
 
 def test_fp32_forward_small_ragged():

@@ -798,6 +798,20 @@ def test_profile_summaries_parse_and_track_the_sources(tmp_path):
     assert rec2 != profiling.source_hash()
 
 
+def test_source_hash_follows_code_not_comments():
+    """Counter summaries stay valid across comment edits and go stale on code edits."""
+    from factorized_block_sparse_amd import profiling
+    a = "int f(int x) {  // twice\n  return 2 * x; /* doubled */ }\n"
+    b = "/* a new remark */\nint f(int x) {\n  return 2 * x;  // the double\n}"
+    assert profiling.code_text(a) == profiling.code_text(b) == "int f(int x) { return 2 * x; }"
+    assert profiling.code_text(a) != profiling.code_text(a.replace("2 * x", "3 * x"))
+    for rel in profiling.SOURCES:  # no comment markers inside string literals
+        text = open(os.path.join(ROOT, rel), encoding="utf-8").read()
+        for line in text.splitlines():
+            code = line.split("//")[0]
+            assert code.count('"') % 2 == 0 or "//" not in line, (rel, line)
+
+
 @pytest.mark.parametrize("n,bq,bk,l", [(300, 64, 32, 7), (1024, 32, 32, 32), (700, 128, 64, 24),
                                        (97, 32, 64, 10), (40, 64, 64, 1), (130, 64, 64, 500)])
 def test_strided_merged_parts_are_disjoint_layouts_of_the_union(n, bq, bk, l):
