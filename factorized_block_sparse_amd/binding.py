@@ -419,7 +419,7 @@ def sparse_attn_bwd(layout: Layout, q, k, v, o, lse, do, scale: float | None = N
                     workspace=None, grads=None, phases: int = SA_BWD_ALL):
     """Backward on the current torch stream: returns (dq, dk, dv).
 
-    ``phases`` selects which of the three launches run (see
+    ``phases`` selects which of the backward's launches run (see
     ``sparse_attn_bwd_phases`` in the C header); the default runs all.
     ``workspace``: a uint8 device tensor of at least ``bwd_workspace_bytes``
     bytes (allocated when omitted).
